@@ -1,0 +1,49 @@
+"""Builds the oracle's page pool for a workload (test infrastructure).
+
+The pool starts as NaN everywhere, pages named by a block table are then filled with
+the poison value, and the workload's history and (optionally) this step's tokens are
+appended with the oracle's own append."""
+import numpy as np
+
+import oracle
+import workloads
+
+
+def scales(wl):
+    if wl.kv_dtype != "fp8":
+        return None, None, None, None
+    return wl.fp8_scales()
+
+
+def oracle_pool(wl, include_step=True):
+    nan, poison = workloads.fill_bits(wl.kv_dtype)
+    pool = oracle.new_pool(wl.num_pages, wl.num_kv_heads, wl.page_size, wl.head_dim,
+                           wl.kv_dtype, fill=nan)
+    pool[wl.referenced_pages()] = poison
+    ks, vs, kinv, vinv = scales(wl)
+    for rows, ctx, new, k, v in wl.history_plan():
+        oracle.append(pool, wl.block_tables[rows], ctx, new, k, v, wl.in_dtype, wl.kv_dtype,
+                      kinv, vinv)
+    if include_step:
+        k, v = wl.step_kv()
+        oracle.append(pool, wl.block_tables, wl.context_lens, wl.new_lens, k, v, wl.in_dtype,
+                      wl.kv_dtype, kinv, vinv)
+    return pool
+
+
+def oracle_outputs(wl, pool):
+    """(decode_out, decode_lse, prefill_out, prefill_lse) for the workload, float64.
+    Decode covers sequences [num_prefill, S); prefill covers [0, num_prefill)."""
+    ks, vs, _, _ = scales(wl)
+    q = wl.q_packed()
+    npf = wl.num_prefill
+    cu = wl.cu(wl.new_lens)
+    pf = (None, None)
+    if npf:
+        pf = oracle.prefill_chunk(pool, wl.block_tables[:npf], wl.context_lens[:npf],
+                                  cu[:npf + 1], q[:cu[npf]], wl.q_dtype, wl.sm_scale,
+                                  wl.kv_dtype, ks, vs)
+    dq = q[cu[npf]:]
+    dec = oracle.decode(pool, wl.block_tables[npf:], wl.context_lens[npf:], dq, wl.q_dtype,
+                        wl.sm_scale, wl.kv_dtype, ks, vs)
+    return dec[0], dec[1], pf[0], pf[1]
