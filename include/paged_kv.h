@@ -1,0 +1,180 @@
+/*
+ * paged_kv.h -- C ABI of libpagedkv.so: attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (by title):
+ *   [Deep dive]  "NVIDIA TensorRT-LLM详解：架构、KV Cache、调度与部署实践"
+ *   [Concept]    "TensorRT-LLM" (concept explainer)
+ *
+ * The KV cache of one attention layer is a pool of fixed-size pages; a sequence's
+ * block table maps its logical page i to a physical page, and pages are handed out
+ * as the sequence grows ([Deep dive] §9, the logical-block -> physical-block
+ * figure; [Concept] 关键机制, PagedAttention).  The page size is a power of two
+ * greater than 1 ([Deep dive] §9, the block-pool facts).  Each engine step hands
+ * the kernels the positions and page tables of the batch ([Concept] 技术原理,
+ * 运行时执行模型, step 2), packed without padding, context (prefill) requests
+ * before generation requests ([Deep dive] §6).
+ *
+ * Conventions for every entry point
+ *   - Pointers named in a struct or argument are DEVICE pointers unless marked
+ *     HOST.  The caller owns every buffer; the library never allocates, frees or
+ *     synchronizes.  Buffers must stay alive until the stream passes the launch.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on it and returns.
+ *   - Return value: PKV_OK (0) or a negative pkv_status_t.  Every precondition the
+ *     host can check is checked before anything is launched; on error nothing is
+ *     enqueued and paged_kv_last_error() describes the problem.
+ *   - Values the host cannot see (page ids inside a block table, device-side
+ *     lengths) must satisfy the stated contract; a violation is undefined
+ *     behaviour (typically a memory fault), exactly as an out-of-range index into
+ *     any device array.
+ *   - Calls are reentrant: the library keeps no state but cached device
+ *     properties and a thread-local error string.
+ */
+#ifndef PAGED_KV_H
+#define PAGED_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_F32 = 0,       /* IEEE binary32 */
+  PKV_BF16 = 1,      /* bfloat16 */
+  PKV_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn": bias 7, max 448, S.1111.111 = NaN) */
+} pkv_dtype_t;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* a null pointer, a bad size or an inconsistent argument */
+  PKV_EUNSUPPORTED = -2,  /* a valid combination this build has no kernel for */
+  PKV_EWORKSPACE = -3,    /* workspace missing or smaller than the size function says */
+  PKV_ELAUNCH = -4        /* the HIP runtime refused the launch */
+} pkv_status_t;
+
+/* One layer's page pool.
+ *   pool: [num_pages][2][num_kv_heads][page_size][head_dim] elements of
+ *         cache_dtype; index 0 of the second axis is K, 1 is V.  A page is the
+ *         K and V of page_size consecutive tokens of one sequence.  16-byte aligned.
+ *   page_size: power of two, >= 2.     head_dim: 64 or 128.
+ *   k_scale / v_scale: FP8 only, [num_kv_heads] float32 dequantization
+ *         multipliers (value = decoded code * scale); NULL for F32/BF16 caches.
+ *   k_inv_scale / v_inv_scale: FP8 only, [num_kv_heads] float32 quantization
+ *         multipliers used by kv_append (code = e4m3(f32(x * inv_scale)));
+ *         NULL for F32/BF16 caches.
+ * FP8 caches hold one scale per (layer, kv head) for K and for V ([Deep dive]
+ * §13, KvCacheConfig(dtype="fp8"); [Concept] 关键机制, 量化方案: FP8 data is
+ * widened back to 16 bits before accumulation). */
+typedef struct pkv_cache {
+  void* pool;
+  int64_t num_pages;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t cache_dtype; /* pkv_dtype_t */
+  const float* k_scale;
+  const float* v_scale;
+  const float* k_inv_scale;
+  const float* v_inv_scale;
+} pkv_cache_t;
+
+/* The sequences of one call.
+ *   block_tables: [num_seqs][max_pages_per_seq] int32, physical page of each
+ *         logical page; entries past a sequence's last page are ignored (-1 by
+ *         convention).  Every entry a call reads must lie in [0, num_pages).
+ *   context_lens: [num_seqs] int32, tokens in the cache AFTER this step's append,
+ *         1 <= context_lens[s] <= max_context_len.
+ *   max_context_len: HOST value, an upper bound of context_lens used to size the
+ *         grid; must satisfy max_context_len <= max_pages_per_seq * page_size. */
+typedef struct pkv_seqs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t max_pages_per_seq;
+  int32_t max_context_len;
+  int32_t reserved; /* must be 0 */
+} pkv_seqs_t;
+
+/* kv_append -- write this step's new K/V rows into the slots the block tables name
+ * ([Deep dive] §2: a decode step writes the new token's KV; §8: each prefill
+ * chunk adds its KV to the cache; [Concept] 技术原理, 调度策略嵌入: the page-table
+ * lookup in front of every KV read and write).
+ *   k_new, v_new: packed [total_new][num_kv_heads][head_dim]; F32 for an F32
+ *         cache, BF16 for BF16 and FP8 caches.
+ *   cu_new_lens: [num_seqs + 1] int32 prefix sums (cu[0] = 0, cu[num_seqs] =
+ *         total_new); sequence s writes rows cu[s] .. cu[s+1]-1 to positions
+ *         context_lens[s] - n_s .. context_lens[s] - 1, n_s = cu[s+1] - cu[s].
+ *   total_new: HOST value, rows in k_new / v_new (0 is a no-op).
+ * Position t of sequence s lands in page block_tables[s][t / page_size], slot
+ * t % page_size.  F32 and BF16 rows are copied bit for bit; an FP8 cache stores
+ * e4m3(f32(x * inv_scale[head])) rounded to nearest-even and saturated to +-448.
+ * Two rows of one call must not name the same slot. */
+int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_new,
+              const void* v_new, const int32_t* cu_new_lens, int32_t total_new,
+              void* stream);
+
+/* Workspace bytes paged_attn_decode needs for these arguments (0 when the call
+ * runs as one partition per sequence).  Same argument rules as the call. */
+size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
+                                        int32_t num_q_heads, int32_t num_splits);
+
+/* paged_attn_decode -- one generation step: each query head of sequence s attends
+ * to all context_lens[s] cached tokens, the one appended this step included
+ * ([Deep dive] §2: decode reads the whole KV history each step).
+ *   q: [num_seqs][num_q_heads][head_dim] of q_dtype (F32 or BF16).
+ *   num_q_heads: a multiple of num_kv_heads; query head h reads kv head
+ *         h / (num_q_heads / num_kv_heads).
+ *   sm_scale: logit scale (1/sqrt(head_dim) in the usual model).
+ *   num_splits: 0 = the library picks page-aligned partitions per sequence; N > 0
+ *         = split each sequence's keys into N equal page-aligned partitions of
+ *         ceil(max_context_len / N) rounded up to a page.  Partitions are merged
+ *         by log-sum-exp (exact up to rounding).
+ *   out: [num_seqs][num_q_heads][head_dim] of q_dtype.
+ *   lse_out: NULL or [num_seqs][num_q_heads] float32, natural-log sum of exp of
+ *         the scaled logits.
+ *   workspace: device buffer of at least paged_attn_decode_workspace_size()
+ *         bytes, 256-byte aligned (NULL allowed when that size is 0).
+ * Results depend only on logical positions: permuting physical pages (and the
+ * tables with them) gives bit-identical output. */
+int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
+                      int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                      int32_t num_splits, void* out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* paged_attn_prefill_chunk -- causal attention of prompt chunks against the cache
+ * the chunks were just appended to ([Deep dive] §8, chunked prefill: every chunk
+ * but the last is a multiple of the block size; §6: context requests are packed
+ * first).  Query i of sequence s sits at position context_lens[s] - C_s + i and
+ * attends to keys 0 .. that position.
+ *   q: packed [total_q][num_q_heads][head_dim] of q_dtype (BF16).
+ *   cu_q_lens: [num_seqs + 1] int32 prefix sums of the chunk lengths C_s, with
+ *         C_s <= context_lens[s].
+ *   total_q, max_q_len: HOST values (rows of q; an upper bound of C_s).
+ *   out: [total_q][num_q_heads][head_dim] of q_dtype; lse_out: NULL or
+ *         [total_q][num_q_heads] float32.
+ *   workspace: unused by this build (pass NULL, 0). */
+int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
+                             const void* q, int32_t q_dtype, const int32_t* cu_q_lens,
+                             int32_t total_q, int32_t max_q_len, int32_t num_q_heads,
+                             float sm_scale, void* out, float* lse_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* paged_kv_debug_gather -- copy every cached token back into logical order, for
+ * checking page addressing bit for bit.  Uses the same page-address code as the
+ * attention kernels.
+ *   k_out, v_out: [num_seqs][max_context_len][num_kv_heads][head_dim] of
+ *         cache_dtype; rows t >= context_lens[s] are left untouched. */
+int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void* k_out,
+                          void* v_out, void* stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* paged_kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_H */

@@ -1,0 +1,160 @@
+"""Python binding of libpagedkv.so (ctypes).
+
+Argument marshalling only: every function here hands device pointers from torch
+tensors, plain sizes and the current HIP stream to the C entry point of the same
+name, and turns a negative status into PagedKVError.  All computation happens in the
+library's HIP kernels; there is no fallback.  Loading fails loudly when the library
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PKV_F32, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ELAUNCH = 0, -1, -2, -3, -4
+STATUS_NAMES = {-1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE", -4: "PKV_ELAUNCH"}
+
+# torch storage dtype of each cache dtype (FP8 codes are kept as raw bytes)
+TORCH_DTYPE = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}
+DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+EXPORTS = ("kv_append", "paged_attn_decode_workspace_size", "paged_attn_decode",
+           "paged_attn_prefill_chunk", "paged_kv_debug_gather", "paged_kv_last_error")
+
+
+class PkvCache(ctypes.Structure):
+    _fields_ = [("pool", c_void_p), ("num_pages", c_int64), ("page_size", c_int32),
+                ("num_kv_heads", c_int32), ("head_dim", c_int32), ("cache_dtype", c_int32),
+                ("k_scale", c_void_p), ("v_scale", c_void_p), ("k_inv_scale", c_void_p),
+                ("v_inv_scale", c_void_p)]
+
+
+class PkvSeqs(ctypes.Structure):
+    _fields_ = [("block_tables", c_void_p), ("context_lens", c_void_p), ("num_seqs", c_int32),
+                ("max_pages_per_seq", c_int32), ("max_context_len", c_int32),
+                ("reserved", c_int32)]
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m paged_kv_cache_413_amd.build)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.kv_append.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
+    lib.kv_append.restype = c_int32
+    lib.paged_attn_decode_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32]
+    lib.paged_attn_decode_workspace_size.restype = c_size_t
+    lib.paged_attn_decode.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
+                                      c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.paged_attn_decode.restype = c_int32
+    lib.paged_attn_prefill_chunk.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_void_p,
+                                             c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
+                                             c_void_p, c_size_t, c_void_p]
+    lib.paged_attn_prefill_chunk.restype = c_int32
+    lib.paged_kv_debug_gather.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_void_p, c_void_p]
+    lib.paged_kv_debug_gather.restype = c_int32
+    lib.paged_kv_last_error.argtypes = []
+    lib.paged_kv_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PKV_OK:
+        raise PagedKVError(status, load().paged_kv_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return c_void_p(stream.cuda_stream)
+    return c_void_p(stream)
+
+
+def make_cache(pool: torch.Tensor, page_size: int, num_kv_heads: int, head_dim: int,
+               cache_dtype: int, k_scale=None, v_scale=None, k_inv_scale=None,
+               v_inv_scale=None) -> PkvCache:
+    """Describe a pool tensor [num_pages][2][num_kv_heads][page_size][head_dim]."""
+    assert pool.is_contiguous() and pool.dim() == 5
+    return PkvCache(_ptr(pool), pool.shape[0], page_size, num_kv_heads, head_dim, cache_dtype,
+                    _ptr(k_scale), _ptr(v_scale), _ptr(k_inv_scale), _ptr(v_inv_scale))
+
+
+def make_seqs(block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int) -> PkvSeqs:
+    """Describe int32 block tables [S][max_pages] and context lengths [S]."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert block_tables.is_contiguous() and context_lens.is_contiguous()
+    S = context_lens.shape[0]
+    return PkvSeqs(_ptr(block_tables), _ptr(context_lens), S,
+                   block_tables.shape[1] if block_tables.dim() == 2 else 0, int(max_context_len), 0)
+
+
+def kv_append(cache: PkvCache, seqs: PkvSeqs, k_new, v_new, cu_new_lens, total_new: int,
+              stream=None):
+    _check(load().kv_append(ctypes.byref(cache), ctypes.byref(seqs), _ptr(k_new), _ptr(v_new),
+                            _ptr(cu_new_lens), int(total_new), _stream(stream)))
+
+
+def paged_attn_decode_workspace_size(cache: PkvCache, seqs: PkvSeqs, num_q_heads: int,
+                                     num_splits: int = 0) -> int:
+    return int(load().paged_attn_decode_workspace_size(ctypes.byref(cache), ctypes.byref(seqs),
+                                                       int(num_q_heads), int(num_splits)))
+
+
+def paged_attn_decode(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, num_q_heads: int,
+                      sm_scale: float, num_splits: int, out, lse_out=None, workspace=None,
+                      workspace_bytes: int | None = None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().paged_attn_decode(ctypes.byref(cache), ctypes.byref(seqs), _ptr(q), int(q_dtype),
+                                    int(num_q_heads), float(sm_scale), int(num_splits), _ptr(out),
+                                    _ptr(lse_out), _ptr(workspace), int(workspace_bytes),
+                                    _stream(stream)))
+
+
+def paged_attn_prefill_chunk(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, cu_q_lens,
+                             total_q: int, max_q_len: int, num_q_heads: int, sm_scale: float,
+                             out, lse_out=None, workspace=None, workspace_bytes: int = 0,
+                             stream=None):
+    _check(load().paged_attn_prefill_chunk(ctypes.byref(cache), ctypes.byref(seqs), _ptr(q),
+                                           int(q_dtype), _ptr(cu_q_lens), int(total_q),
+                                           int(max_q_len), int(num_q_heads), float(sm_scale),
+                                           _ptr(out), _ptr(lse_out), _ptr(workspace),
+                                           int(workspace_bytes), _stream(stream)))
+
+
+def paged_kv_debug_gather(cache: PkvCache, seqs: PkvSeqs, k_out, v_out, stream=None):
+    _check(load().paged_kv_debug_gather(ctypes.byref(cache), ctypes.byref(seqs), _ptr(k_out),
+                                        _ptr(v_out), _stream(stream)))
+
+
+def paged_kv_last_error() -> str:
+    return load().paged_kv_last_error().decode()

@@ -1,0 +1,285 @@
+// C-ABI front end of libpagedkv: argument validation, partition choice and dispatch.
+// Every host-checkable precondition is checked here, before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/paged_kv.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int ilog2_exact(int v) {
+  if (v < 2 || (v & (v - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute-unit count of the current device, cached per device.
+int cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev >= int(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+int check_cache(const pkv_cache_t* c, pkv::CacheArgs& out) {
+  if (!c) return fail(PKV_EINVAL, "cache is NULL");
+  if (!c->pool) return fail(PKV_EINVAL, "cache->pool is NULL");
+  if (!aligned(c->pool, 16)) return fail(PKV_EINVAL, "cache->pool must be 16-byte aligned");
+  if (c->num_pages < 1) return fail(PKV_EINVAL, "cache->num_pages must be >= 1 (got %lld)", (long long)c->num_pages);
+  const int lp = ilog2_exact(c->page_size);
+  if (lp < 0 || c->page_size > 4096)
+    return fail(PKV_EINVAL, "cache->page_size must be a power of two in [2, 4096] (got %d)", c->page_size);
+  if (c->num_kv_heads < 1) return fail(PKV_EINVAL, "cache->num_kv_heads must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "cache->head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->cache_dtype != PKV_F32 && c->cache_dtype != PKV_BF16 && c->cache_dtype != PKV_FP8_E4M3)
+    return fail(PKV_EINVAL, "cache->cache_dtype %d is not a pkv_dtype_t", c->cache_dtype);
+  out.pool = c->pool;
+  out.num_pages = c->num_pages;
+  out.page_size = c->page_size;
+  out.log2_page = lp;
+  out.num_kv_heads = c->num_kv_heads;
+  out.head_dim = c->head_dim;
+  out.dtype = c->cache_dtype;
+  out.k_scale = c->k_scale;
+  out.v_scale = c->v_scale;
+  out.k_inv_scale = c->k_inv_scale;
+  out.v_inv_scale = c->v_inv_scale;
+  return PKV_OK;
+}
+
+int check_seqs(const pkv_seqs_t* s, const pkv::CacheArgs& c, pkv::SeqArgs& out) {
+  if (!s) return fail(PKV_EINVAL, "seqs is NULL");
+  if (s->reserved != 0) return fail(PKV_EINVAL, "seqs->reserved must be 0");
+  if (s->num_seqs < 0) return fail(PKV_EINVAL, "seqs->num_seqs must be >= 0");
+  out.num_seqs = s->num_seqs;
+  out.block_tables = s->block_tables;
+  out.context_lens = s->context_lens;
+  out.max_pages_per_seq = s->max_pages_per_seq;
+  out.max_context_len = s->max_context_len;
+  if (s->num_seqs == 0) return PKV_OK;
+  if (!s->block_tables) return fail(PKV_EINVAL, "seqs->block_tables is NULL");
+  if (!s->context_lens) return fail(PKV_EINVAL, "seqs->context_lens is NULL");
+  if (s->max_pages_per_seq < 1) return fail(PKV_EINVAL, "seqs->max_pages_per_seq must be >= 1");
+  if (s->max_context_len < 1) return fail(PKV_EINVAL, "seqs->max_context_len must be >= 1");
+  if (int64_t(s->max_context_len) > int64_t(s->max_pages_per_seq) * c.page_size)
+    return fail(PKV_EINVAL, "seqs->max_context_len (%d) exceeds max_pages_per_seq * page_size (%lld)",
+                s->max_context_len, (long long)s->max_pages_per_seq * c.page_size);
+  return PKV_OK;
+}
+
+int check_fp8_scales(const pkv::CacheArgs& c, bool inv) {
+  if (c.dtype != PKV_FP8_E4M3) return PKV_OK;
+  if (inv ? (!c.k_inv_scale || !c.v_inv_scale) : (!c.k_scale || !c.v_scale))
+    return fail(PKV_EINVAL, "an FP8 cache needs %s", inv ? "k_inv_scale and v_inv_scale" : "k_scale and v_scale");
+  return PKV_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct DecodePlan {
+  int chunk, max_splits;
+  size_t ws_o_bytes, ws_bytes;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Page-aligned partitions of the keys.  A fixed N splits max_context_len into N equal
+// page-aligned parts; the automatic choice aims at a few work items per compute unit
+// (estimated from max_context_len, the only length the host knows), never cutting
+// below 256 keys, and stays a single partition when that already gives enough work.
+DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
+                       int num_splits) {
+  const int P = c.page_size;
+  const int64_t maxL = s.max_context_len;
+  int64_t chunk;
+  if (num_splits > 0) {
+    chunk = cdiv(cdiv(maxL, num_splits), P) * P;
+  } else {
+    const int64_t target = 8LL * cu_count();
+    const int64_t est = cdiv(int64_t(s.num_seqs) * c.num_kv_heads * maxL, target);
+    chunk = cdiv(std::max<int64_t>(est, std::max(256, P)), P) * P;
+  }
+  chunk = std::min<int64_t>(std::max<int64_t>(chunk, P), cdiv(maxL, P) * P);
+  DecodePlan p;
+  p.chunk = int(chunk);
+  p.max_splits = int(cdiv(maxL, chunk));
+  if (p.max_splits <= 1) {
+    p.max_splits = 1;
+    p.ws_o_bytes = p.ws_bytes = 0;
+  } else {
+    const size_t slots = size_t(s.num_seqs) * num_q_heads * p.max_splits;
+    p.ws_o_bytes = align256(slots * c.head_dim * sizeof(float));
+    p.ws_bytes = p.ws_o_bytes + align256(slots * sizeof(float));
+  }
+  return p;
+}
+
+int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads) {
+  if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "q_dtype must be PKV_F32 or PKV_BF16 (got %d)", q_dtype);
+  if (num_q_heads < 1 || num_q_heads % c.num_kv_heads)
+    return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, c.num_kv_heads);
+  const int G = num_q_heads / c.num_kv_heads;
+  if (!pkv::valu_supported(c.dtype, q_dtype, c.head_dim, G))
+    return fail(PKV_EUNSUPPORTED, "no kernel for cache dtype %d, q dtype %d, head_dim %d, group %d",
+                c.dtype, q_dtype, c.head_dim, G);
+  return check_fp8_scales(c, false);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_kv_last_error(void) { return g_error.c_str(); }
+
+int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_new,
+              const void* v_new, const int32_t* cu_new_lens, int32_t total_new, void* stream) {
+  pkv::CacheArgs c;
+  pkv::SeqArgs s;
+  int st;
+  if ((st = check_cache(cache, c)) != PKV_OK) return st;
+  if ((st = check_seqs(seqs, c, s)) != PKV_OK) return st;
+  if (total_new < 0) return fail(PKV_EINVAL, "total_new must be >= 0");
+  if (total_new == 0 || s.num_seqs == 0) return ok();
+  if (!k_new || !v_new || !cu_new_lens) return fail(PKV_EINVAL, "k_new, v_new and cu_new_lens must not be NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if ((st = check_fp8_scales(c, true)) != PKV_OK) return st;
+  const int in_dtype = c.dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
+  return launch_status(pkv::launch_kv_append(c, s, k_new, v_new, in_dtype, cu_new_lens, total_new,
+                                             static_cast<hipStream_t>(stream)),
+                       "kv_append");
+}
+
+size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
+                                        int32_t num_q_heads, int32_t num_splits) {
+  pkv::CacheArgs c;
+  pkv::SeqArgs s;
+  if (check_cache(cache, c) != PKV_OK || check_seqs(seqs, c, s) != PKV_OK) return 0;
+  if (s.num_seqs == 0 || num_q_heads < 1 || num_splits < 0) return 0;
+  return plan_decode(c, s, num_q_heads, num_splits).ws_bytes;
+}
+
+int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
+                      int32_t q_dtype, int32_t num_q_heads, float sm_scale, int32_t num_splits,
+                      void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  pkv::AttnArgs a{};
+  int st;
+  if ((st = check_cache(cache, a.cache)) != PKV_OK) return st;
+  if ((st = check_seqs(seqs, a.cache, a.seqs)) != PKV_OK) return st;
+  if ((st = check_attn(a.cache, q_dtype, num_q_heads)) != PKV_OK) return st;
+  if (num_splits < 0) return fail(PKV_EINVAL, "num_splits must be >= 0");
+  if (a.seqs.num_seqs == 0) return ok();
+  if (!q || !out) return fail(PKV_EINVAL, "q and out must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  const DecodePlan p = plan_decode(a.cache, a.seqs, num_q_heads, num_splits);
+  if (p.ws_bytes) {
+    if (!workspace || workspace_bytes < p.ws_bytes)
+      return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                  workspace ? workspace_bytes : size_t(0));
+    if (!aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  }
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.num_q_heads = num_q_heads;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.chunk = p.chunk;
+  a.max_splits = p.max_splits;
+  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
+  return launch_status(pkv::launch_valu_decode(a, static_cast<hipStream_t>(stream)), "paged_attn_decode");
+}
+
+int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
+                             int32_t q_dtype, const int32_t* cu_q_lens, int32_t total_q,
+                             int32_t max_q_len, int32_t num_q_heads, float sm_scale, void* out,
+                             float* lse_out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  pkv::AttnArgs a{};
+  int st;
+  if ((st = check_cache(cache, a.cache)) != PKV_OK) return st;
+  if ((st = check_seqs(seqs, a.cache, a.seqs)) != PKV_OK) return st;
+  if ((st = check_attn(a.cache, q_dtype, num_q_heads)) != PKV_OK) return st;
+  if (total_q < 0 || max_q_len < 0) return fail(PKV_EINVAL, "total_q and max_q_len must be >= 0");
+  if (a.seqs.num_seqs == 0 || total_q == 0) return ok();
+  if (!q || !out || !cu_q_lens) return fail(PKV_EINVAL, "q, out and cu_q_lens must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
+  if (max_q_len < 1 || max_q_len > a.seqs.max_context_len)
+    return fail(PKV_EINVAL, "max_q_len (%d) must be in [1, max_context_len]", max_q_len);
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.num_q_heads = num_q_heads;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.cu_q_lens = cu_q_lens;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.chunk = int(cdiv(a.seqs.max_context_len, a.cache.page_size) * a.cache.page_size);
+  a.max_splits = 1;
+  return launch_status(pkv::launch_valu_prefill(a, static_cast<hipStream_t>(stream)),
+                       "paged_attn_prefill_chunk");
+}
+
+int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void* k_out,
+                          void* v_out, void* stream) {
+  pkv::CacheArgs c;
+  pkv::SeqArgs s;
+  int st;
+  if ((st = check_cache(cache, c)) != PKV_OK) return st;
+  if ((st = check_seqs(seqs, c, s)) != PKV_OK) return st;
+  if (s.num_seqs == 0) return ok();
+  if (s.num_seqs > 65535) return fail(PKV_EUNSUPPORTED, "debug gather handles at most 65535 sequences");
+  if (!k_out || !v_out) return fail(PKV_EINVAL, "k_out and v_out must not be NULL");
+  if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(PKV_EINVAL, "k_out and v_out must be 16-byte aligned");
+  return launch_status(pkv::launch_debug_gather(c, s, k_out, v_out, static_cast<hipStream_t>(stream)),
+                       "paged_kv_debug_gather");
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Device helpers shared by every kernel of libpagedkv: page addressing and element
+// conversions.  gfx950 (CDNA4), wave64.
+//
+// Page addressing ("NVIDIA TensorRT-LLM详解：架构、KV Cache、调度与部署实践", §9: a
+// request's logical blocks map to physical blocks through its block table):
+// logical token t of a sequence lives in physical page block_table[t >> log2P] at
+// slot t & (P - 1); the pool is [page][K|V][kv_head][slot][dim], so one (page, K|V,
+// kv_head) tile is P*D contiguous elements and one token row is D contiguous ones.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element offset of tile (page, kv, head) in the pool.
+__device__ __forceinline__ int64_t tile_offset(int32_t page, int kv, int head, int num_kv_heads,
+                                               int page_size, int head_dim) {
+  return ((int64_t(page) * 2 + kv) * num_kv_heads + head) * int64_t(page_size) * head_dim;
+}
+
+// Element offset of token t's row (kv, head) for the sequence whose table row is bt.
+__device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ bt, int t, int log2P,
+                                              int kv, int head, int num_kv_heads, int head_dim) {
+  const int32_t page = bt[t >> log2P];
+  const int slot = t & ((1 << log2P) - 1);
+  return tile_offset(page, kv, head, num_kv_heads, 1 << log2P, head_dim) + int64_t(slot) * head_dim;
+}
+
+__device__ __forceinline__ int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }
+
+// ---- bfloat16 ------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- OCP FP8 E4M3 --------------------------------------------------------------------
+// Decode two codes (bytes 0,1 when hi == false, bytes 2,3 when true) of a 32-bit word
+// with gfx950's conversion, which implements the OCP E4M3 format.
+__device__ __forceinline__ void fp8x2_to_f32(uint32_t w, bool hi, float& a, float& b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  f2 r = hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  a = r[0];
+  b = r[1];
+}
+
+// Encode one float32 value as E4M3: round to nearest, ties to even mantissa;
+// magnitudes >= 448 and infinities saturate to +-448; NaN -> S.1111.111.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;          // >= 448.0f
+  if (a >= 0x3c800000u) {                              // >= 2^-6: normal E4M3
+    // keep 3 of the 23 mantissa bits, rounding to nearest even; a carry moves into
+    // the exponent, which is what rounding up to the next binade needs
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+    return sign | (r - (120u << 3));                   // rebias 127 -> 7
+  }
+  // subnormal E4M3: code = m with value m * 2^-9, m = rint(|v| * 2^9) in [0, 8]
+  // (|v| * 512 is exact; 8 is the smallest normal code, 0x08)
+  const float t = __uint_as_float(a) * 512.0f;
+  return sign | uint32_t(__builtin_rintf(t));
+}
+
+}  // namespace pkv

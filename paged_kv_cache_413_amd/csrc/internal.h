@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI front end (api.cpp) and the kernel
+// translation units.  Arguments are validated by the front end before any launcher
+// is called; launchers only enqueue work and return the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct CacheArgs {
+  void* pool;
+  int64_t num_pages;
+  int page_size, log2_page, num_kv_heads, head_dim, dtype;
+  const float *k_scale, *v_scale, *k_inv_scale, *v_inv_scale;
+};
+
+struct SeqArgs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, max_pages_per_seq, max_context_len;
+};
+
+// kv_append
+hipError_t launch_kv_append(const CacheArgs& c, const SeqArgs& s, const void* k_new,
+                            const void* v_new, int in_dtype, const int32_t* cu_new_lens,
+                            int total_new, hipStream_t stream);
+
+// Attention.  Rows are decode sequences (cu_q_lens == nullptr: row r = sequence r,
+// keys 0..context_lens[r]-1) or packed prefill queries (row r = query i of the
+// sequence s with cu_q_lens[s] <= r < cu_q_lens[s+1]; keys 0..L_s - C_s + i).
+struct AttnArgs {
+  CacheArgs cache;
+  SeqArgs seqs;
+  const void* q;
+  int q_dtype, num_q_heads;
+  float sm_scale;
+  void* out;
+  float* lse_out;
+  const int32_t* cu_q_lens;  // prefill only
+  int total_q, max_q_len;    // prefill only
+  // split-KV (decode): partitions of `chunk` tokens (a multiple of the page size)
+  int chunk, max_splits;
+  float* ws_o;    // [rows][Hq][max_splits][D] normalised partial outputs
+  float* ws_lse;  // [rows][Hq][max_splits] partial log-sum-exp
+};
+
+// General vector-ALU kernels (attn_valu.hip): every supported combination.
+bool valu_supported(int kv_dtype, int q_dtype, int head_dim, int group);
+hipError_t launch_valu_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_valu_prefill(const AttnArgs& a, hipStream_t stream);
+
+// Debug gather
+hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,
+                               hipStream_t stream);
+
+}  // namespace pkv

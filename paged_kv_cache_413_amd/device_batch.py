@@ -1,0 +1,159 @@
+"""A workload's batch resident on the GPU, driven through the C ABI.
+
+Holds the page pool, block tables, lengths, queries and this step's new K/V as torch
+device tensors and runs one step of the hot path on one stream:
+
+    kv_append (all sequences: prefill chunks first, then one token per decode
+    sequence)  ->  paged_attn_prefill_chunk (prefill requests)  ->
+    paged_attn_decode (decode sequences)
+
+The pool starts as NaN, pages named by a block table are filled with a large
+finite poison, and the history is written with kv_append itself, so every byte the
+attention kernels read was placed by the library.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads
+from . import binding as B
+
+KV_CODE = {"f32": B.PKV_F32, "bf16": B.PKV_BF16, "fp8": B.PKV_FP8_E4M3}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
+VAL_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Storage array (float32, or bf16 bits as uint16) -> torch tensor on device."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def _bits_scalar(v) -> int:
+    a = np.asarray(v)
+    if a.dtype == np.float32:
+        return int(a.view(np.int32))
+    if a.dtype == np.uint16:
+        return int(a.view(np.int16))
+    return int(a)
+
+
+class DeviceBatch:
+    def __init__(self, wl: workloads.Workload, device="cuda:0", num_splits: int | None = None):
+        self.wl = wl
+        self.dev = torch.device(device)
+        self.kv_code = KV_CODE[wl.kv_dtype]
+        self.q_code = B.PKV_F32 if wl.q_dtype == "f32" else B.PKV_BF16
+        self.num_splits = wl.num_splits if num_splits is None else num_splits
+        dev = self.dev
+        Hkv, P, D = wl.num_kv_heads, wl.page_size, wl.head_dim
+        self.pool = torch.empty((wl.num_pages, 2, Hkv, P, D), dtype=VAL_DTYPE[wl.kv_dtype], device=dev)
+        nan, poison = workloads.fill_bits(wl.kv_dtype)
+        iv = self.pool.view(INT_VIEW[wl.kv_dtype])
+        iv.fill_(_bits_scalar(nan))
+        ref = torch.from_numpy(wl.referenced_pages().astype(np.int64)).to(dev)
+        iv.index_fill_(0, ref, _bits_scalar(poison))
+        self.block_tables = torch.from_numpy(wl.block_tables).to(dev)
+        self.context_lens = torch.from_numpy(wl.context_lens).to(dev)
+        self.scales = [None] * 4
+        if wl.kv_dtype == "fp8":
+            self.scales = [torch.from_numpy(x).to(dev) for x in wl.fp8_scales()]
+        self.cache = B.make_cache(self.pool, P, Hkv, D, self.kv_code, *self.scales)
+        self.npf = wl.num_prefill
+        self._step_ready = False
+
+    # ---- history ---------------------------------------------------------------------
+    def fill_history(self):
+        wl = self.wl
+        for rows, ctx, new, k, v in wl.history_plan():
+            rows_t = torch.from_numpy(rows.astype(np.int64)).to(self.dev)
+            bt = self.block_tables.index_select(0, rows_t).contiguous()
+            ctx_t = torch.from_numpy(ctx).to(self.dev)
+            cu = torch.from_numpy(wl.cu(new)).to(self.dev)
+            kd, vd = to_device(k, wl.in_dtype, self.dev), to_device(v, wl.in_dtype, self.dev)
+            seqs = B.make_seqs(bt, ctx_t, int(ctx.max()))
+            B.kv_append(self.cache, seqs, kd, vd, cu, int(new.sum()))
+            torch.cuda.synchronize(self.dev)
+            del kd, vd
+
+    # ---- one step ----------------------------------------------------------------------
+    def prepare_step(self):
+        wl = self.wl
+        dev = self.dev
+        npf = self.npf
+        cu_all = wl.cu(wl.new_lens)
+        self.q = to_device(wl.q_packed(), wl.q_dtype, dev)
+        k, v = wl.step_kv()
+        self.k_new = to_device(k, wl.in_dtype, dev)
+        self.v_new = to_device(v, wl.in_dtype, dev)
+        self.cu_new = torch.from_numpy(cu_all).to(dev)
+        self.total_new = int(cu_all[-1])
+        self.seqs_all = B.make_seqs(self.block_tables, self.context_lens, wl.max_context_len)
+        Hq, D = wl.num_q_heads, wl.head_dim
+        qdt = VAL_DTYPE[wl.q_dtype]
+        # prefill requests: rows [0, npf)
+        self.npf_q = int(cu_all[npf])
+        if npf:
+            self.bt_pf = self.block_tables[:npf]
+            self.ctx_pf = self.context_lens[:npf]
+            self.seqs_pf = B.make_seqs(self.bt_pf, self.ctx_pf, int(wl.context_lens[:npf].max()))
+            self.cu_q = torch.from_numpy(cu_all[:npf + 1].copy()).to(dev)
+            self.q_pf = self.q[:self.npf_q]
+            self.out_pf = torch.empty((self.npf_q, Hq, D), dtype=qdt, device=dev)
+            self.lse_pf = torch.empty((self.npf_q, Hq), dtype=torch.float32, device=dev)
+            self.max_q = int(wl.new_lens[:npf].max())
+        # decode sequences: rows [npf, S)
+        S = wl.num_seqs
+        self.ndec = S - npf
+        self.bt_dec = self.block_tables[npf:]
+        self.ctx_dec = self.context_lens[npf:]
+        self.q_dec = self.q[self.npf_q:]
+        dec_max = int(wl.context_lens[npf:].max()) if self.ndec else 1
+        self.seqs_dec = B.make_seqs(self.bt_dec, self.ctx_dec, dec_max)
+        self.out_dec = torch.empty((self.ndec, Hq, D), dtype=qdt, device=dev)
+        self.lse_dec = torch.empty((self.ndec, Hq), dtype=torch.float32, device=dev)
+        ws = B.paged_attn_decode_workspace_size(self.cache, self.seqs_dec, Hq, self.num_splits) if self.ndec else 0
+        self.ws_dec = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws_dec_bytes = ws
+        self._step_ready = True
+
+    def append_step(self, stream=None):
+        B.kv_append(self.cache, self.seqs_all, self.k_new, self.v_new, self.cu_new, self.total_new,
+                    stream=stream)
+
+    def prefill_step(self, stream=None):
+        if not self.npf:
+            return
+        wl = self.wl
+        B.paged_attn_prefill_chunk(self.cache, self.seqs_pf, self.q_pf, self.q_code, self.cu_q,
+                                   self.npf_q, self.max_q, wl.num_q_heads, float(wl.sm_scale),
+                                   self.out_pf, self.lse_pf, stream=stream)
+
+    def decode_step(self, stream=None, num_splits=None):
+        if not self.ndec:
+            return
+        wl = self.wl
+        ns = self.num_splits if num_splits is None else num_splits
+        B.paged_attn_decode(self.cache, self.seqs_dec, self.q_dec, self.q_code, wl.num_q_heads,
+                            float(wl.sm_scale), ns, self.out_dec, self.lse_dec, self.ws_dec,
+                            self.ws_dec_bytes, stream=stream)
+
+    def step(self, stream=None):
+        """One pass of the hot path: append, then prefill-chunk attention, then decode."""
+        if not self._step_ready:
+            self.prepare_step()
+        self.append_step(stream)
+        self.prefill_step(stream)
+        self.decode_step(stream)
+
+    # ---- results on the host -----------------------------------------------------------
+    def pool_bits(self) -> np.ndarray:
+        return self.pool.view(INT_VIEW[self.wl.kv_dtype]).cpu().numpy()
+
+    def outputs_f64(self):
+        """(decode out, decode lse, prefill out, prefill lse) as float64 NumPy arrays."""
+        f = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+        pf = (f(self.out_pf), f(self.lse_pf)) if self.npf else (None, None)
+        return f(self.out_dec), f(self.lse_dec), pf[0], pf[1]

@@ -1,0 +1,31 @@
+"""Shared helpers of the GPU parity tests: tolerances and comparisons against the
+oracle (test infrastructure)."""
+import numpy as np
+
+# Tolerances: fp32 max-abs 1e-4; bf16 and FP8-KV outputs per (row, head)
+# infinity-norm relative error 2e-2 and 5e-2.  The log-sum-exp is compared in
+# absolute terms: the kernels accumulate it in fp32 from exact bf16/fp8 inputs.
+TOL = {"f32": ("abs", 1e-4), "bf16": ("rel", 2e-2), "fp8": ("rel", 5e-2)}
+LSE_ATOL = {"f32": 1e-4, "bf16": 2e-3, "fp8": 2e-3}
+
+
+def rel_inf(got, ref):
+    """max over (row, head) of ||got - ref||_inf / ||ref||_inf."""
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    return float((num / den).max()) if num.size else 0.0
+
+
+def assert_close(got, ref, kv_dtype, what=""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    kind, tol = TOL[kv_dtype]
+    err = float(np.abs(got - ref).max()) if kind == "abs" else rel_inf(got, ref)
+    assert err <= tol, f"{what}: {kind} error {err:.3e} > {tol:.1e}"
+    return err
+
+
+def assert_lse_close(got, ref, kv_dtype, what=""):
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    assert err <= LSE_ATOL[kv_dtype], f"{what}: lse error {err:.3e}"
+    return err
