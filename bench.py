@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Benchmark of one step of attention over a paged KV cache on one MI355X.
+
+A step is one pass of the hot path over one seeded synthetic batch resident in HBM:
+kv_append of this step's new K/V (one token per decode sequence, whole chunks for
+prefill requests), then causal prefill-chunk attention for prefill requests (if the
+workload has any), then paged decode attention with its split-KV merge.  Every
+kernel runs in libpagedkv.so through its C ABI on torch's current stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line.  `value` is the KV bytes the step's attention reads (K and V
+of every attended token of every sequence) per second of step time.  `roofline`
+rates the dominant launch, paged_attn_decode, against MI355X's 8 TB/s HBM peak
+using its event-timed duration; `cpu_baseline` is the CPU fp64 oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOADS = {
+    "llama3_8b_decode_bf16": 2,
+    "tiny_fp32_decode": 1,
+    "mixed_inflight_bf16": 3,
+    "long_context_splitkv_bf16": 4,
+    "fp8_shared_prefix_decode": 5,
+}
+KERNEL_SOURCES = ("attn_valu.hip", "attn_mfma.hip", "append.hip", "device_common.h", "api.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_413_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        p = os.path.join(csrc, name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per decode launch measured with rocprofv3 counters, if the summary
+    under profiles/ was taken from the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_val) or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes one decode launch must move at minimum: K and V of every attended token
+    (once per sequence), the queries and outputs, the block-table entries the
+    sequences use and their lengths."""
+    import numpy as np
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    qel = 4 if wl.q_dtype == "f32" else 2
+    npf = wl.num_prefill
+    L = wl.context_lens[npf:].astype(np.int64)
+    S = len(L)
+    kv = int(L.sum()) * 2 * wl.num_kv_heads * wl.head_dim * elem
+    qo = 2 * S * wl.num_q_heads * wl.head_dim * qel
+    bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + S * 4
+    return {"kv": kv, "total": kv + qo + bt}
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The CPU fp64 oracle on a bounded sample of the workload's decode sequences:
+    this step's append into an oracle pool holding those sequences' history, then
+    their decode attention.  Returns the dict for the JSON line."""
+    import numpy as np
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    npf = wl.num_prefill
+    order = list(range(npf, wl.num_seqs))
+    scales = wl.fp8_scales() if wl.kv_dtype == "fp8" else (None, None, None, None)
+    ks, vs, kinv, vinv = scales
+    _, poison = _fill(wl)
+    q_all = wl.q_packed()
+    cu = wl.cu(wl.new_lens)
+    elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    done, bytes_done, t_spent = [], 0, 0.0
+    for s in order:
+        # a compact pool holding sequence s's pages only, with its table renumbered
+        # (the oracle's result does not depend on physical page ids)
+        row = wl.block_tables[s]
+        used = row[row >= 0]
+        table = np.full((1, len(row)), -1, np.int32)
+        table[0, :len(used)] = np.arange(len(used), dtype=np.int32)
+        pool = oracle.new_pool(len(used), wl.num_kv_heads, wl.page_size, wl.head_dim,
+                               wl.kv_dtype, fill=poison)
+        L, n = int(wl.context_lens[s]), int(wl.new_lens[s])
+        k_hist, v_hist = wl.tokens(s, 0, L - n)
+        rows = np.array([s])
+        if L - n:
+            oracle.append(pool, table, np.array([L - n]), np.array([L - n]),
+                          k_hist, v_hist, wl.in_dtype, wl.kv_dtype, kinv, vinv)
+        k_new, v_new = wl.tokens(s, L - n, L)
+        q = q_all[cu[s]:cu[s + 1]]
+        t0 = time.perf_counter()
+        oracle.append(pool, table, wl.context_lens[rows], wl.new_lens[rows],
+                      k_new, v_new, wl.in_dtype, wl.kv_dtype, kinv, vinv)
+        oracle.decode(pool, table, wl.context_lens[rows], q, wl.q_dtype,
+                      wl.sm_scale, wl.kv_dtype, ks, vs)
+        t_spent += time.perf_counter() - t0
+        done.append(s)
+        bytes_done += L * 2 * wl.num_kv_heads * wl.head_dim * elem
+        del pool
+        if t_spent >= budget_s:
+            break
+    gbs = bytes_done / t_spent / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{len(done)} of {wl.num_seqs - npf} decode sequences of {wl.name} "
+                       f"({bytes_done / 1e6:.1f} MB of KV, {t_spent:.1f} s): kv_append of the "
+                       f"step's token then fp64 decode attention, history preloaded untimed"),
+            "seconds": round(t_spent, 3)}
+
+
+def _fill(wl):
+    import workloads
+    return workloads.fill_bits(wl.kv_dtype)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="override the workload's partition count (0 = library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_cache_413_amd import binding
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()  # raises when libpagedkv.so is missing: there is no other path
+
+    cfg = WORKLOADS[args.workload]
+    t_setup = time.perf_counter()
+    wl = workloads.make(cfg)
+    wl.prefetch()
+    db = DeviceBatch(wl, device="cuda:0", num_splits=args.num_splits)
+    db.fill_history()
+    db.prepare_step()
+    torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        db.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    E = torch.cuda.Event
+    ev = [[E(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        db.append_step()
+        ev[i][1].record()
+        db.prefill_step()
+        ev[i][2].record()
+        db.decode_step()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / K * 1e3
+
+    append_ms = float(np.mean([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]))
+    prefill_ms = float(np.mean([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]))
+    decode_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
+    decode_min_ms = float(np.min([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]))
+    print(f"[bench] step {ms_step * 1e3:.1f} us: append {append_ms * 1e3:.1f} us, prefill "
+          f"{prefill_ms * 1e3:.1f} us, decode {decode_ms * 1e3:.1f} us (min {decode_min_ms * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
+    ab = algorithmic_bytes(wl)
+    tokens = int(wl.new_lens.sum())
+    kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
+    achieved = ab["total"] / (decode_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(wl.name)
+
+    # one decode launch through the split count the bench used, for the record
+    ns = db.num_splits
+    res = {
+        "metric": "paged decode attention: KV GB/s and % of HBM peak; tokens/s per step",
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.kv_dtype,
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded lengths and page permutation)",
+        "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_prefill": wl.num_prefill,
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "page_size": wl.page_size, "kv_dtype": wl.kv_dtype,
+                   "context_tokens": int(wl.context_lens.sum()), "num_splits": ns,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "hbm_frac_step": round(kv_gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes": ab["kv"],
+        "kernel_us": {"kv_append": round(append_ms * 1e3, 2),
+                      "paged_attn_prefill_chunk": round(prefill_ms * 1e3, 2),
+                      "paged_attn_decode": round(decode_ms * 1e3, 2),
+                      "paged_attn_decode_min": round(decode_min_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab["total"]},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    del db
+    torch.cuda.empty_cache()
+    if args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
