@@ -56,9 +56,14 @@ typedef enum {
 } pkv_status_t;
 
 /* One layer's page pool.
- *   pool: [num_pages][2][num_kv_heads][page_size][head_dim] elements of
- *         cache_dtype; index 0 of the second axis is K, 1 is V.  A page is the
- *         K and V of page_size consecutive tokens of one sequence.  16-byte aligned.
+ *   pool: [num_pages][2][num_kv_heads][tile] elements of cache_dtype, one tile of
+ *         page_size * head_dim elements per (page, K|V, kv head); index 0 of the
+ *         second axis is K, 1 is V.  A page holds the K and V of page_size
+ *         consecutive tokens of one sequence.  16-byte aligned.
+ *           K tile: token-major [page_size][head_dim] (a token's row is contiguous)
+ *           V tile: dim-major   [head_dim][page_size] (a dim's tokens are contiguous)
+ *         V is stored transposed so that the probability-times-V product reads
+ *         consecutive tokens of one dim, the operand layout of the matrix cores.
  *   page_size: power of two, >= 2.     head_dim: 64 or 128.
  *   k_scale / v_scale: FP8 only, [num_kv_heads] float32 dequantization
  *         multipliers (value = decoded code * scale); NULL for F32/BF16 caches.
@@ -117,9 +122,11 @@ int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_ne
               void* stream);
 
 /* Workspace bytes paged_attn_decode needs for these arguments (0 when the call
- * runs as one partition per sequence).  Same argument rules as the call. */
+ * runs as one partition per sequence).  Same argument rules as the call; 0 is also
+ * returned for arguments the call would reject. */
 size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
-                                        int32_t num_q_heads, int32_t num_splits);
+                                        int32_t q_dtype, int32_t num_q_heads,
+                                        int32_t num_splits);
 
 /* paged_attn_decode -- one generation step: each query head of sequence s attends
  * to all context_lens[s] cached tokens, the one appended this step included
@@ -128,10 +135,14 @@ size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs
  *   num_q_heads: a multiple of num_kv_heads; query head h reads kv head
  *         h / (num_q_heads / num_kv_heads).
  *   sm_scale: logit scale (1/sqrt(head_dim) in the usual model).
- *   num_splits: 0 = the library picks page-aligned partitions per sequence; N > 0
- *         = split each sequence's keys into N equal page-aligned partitions of
- *         ceil(max_context_len / N) rounded up to a page.  Partitions are merged
- *         by log-sum-exp (exact up to rounding).
+ *   num_splits: 0 = the library partitions the keys itself: with a BF16 or FP8
+ *         cache, BF16 queries and pages of >= 8 tokens (the matrix-core kernels)
+ *         the 32-token blocks of all (sequence, kv head) pairs are cut into equal
+ *         contiguous shares, one per wave that fits on the device at once;
+ *         otherwise page-aligned partitions of at least 256 keys.  N > 0 = split
+ *         each sequence's keys into page-aligned partitions of ceil(max_context_len
+ *         / N) keys, rounded up to a page (and to 32 keys on the matrix-core
+ *         path).  Partial results are merged by log-sum-exp (exact up to rounding).
  *   out: [num_seqs][num_q_heads][head_dim] of q_dtype.
  *   lse_out: NULL or [num_seqs][num_q_heads] float32, natural-log sum of exp of
  *         the scaled logits.

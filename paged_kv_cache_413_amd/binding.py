@@ -61,7 +61,7 @@ def load(path: str = LIB_PATH):
     P = ctypes.POINTER
     lib.kv_append.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
     lib.kv_append.restype = c_int32
-    lib.paged_attn_decode_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32]
+    lib.paged_attn_decode_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32, c_int32]
     lib.paged_attn_decode_workspace_size.restype = c_size_t
     lib.paged_attn_decode.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
@@ -123,10 +123,11 @@ def kv_append(cache: PkvCache, seqs: PkvSeqs, k_new, v_new, cu_new_lens, total_n
                             _ptr(cu_new_lens), int(total_new), _stream(stream)))
 
 
-def paged_attn_decode_workspace_size(cache: PkvCache, seqs: PkvSeqs, num_q_heads: int,
-                                     num_splits: int = 0) -> int:
+def paged_attn_decode_workspace_size(cache: PkvCache, seqs: PkvSeqs, q_dtype: int,
+                                     num_q_heads: int, num_splits: int = 0) -> int:
     return int(load().paged_attn_decode_workspace_size(ctypes.byref(cache), ctypes.byref(seqs),
-                                                       int(num_q_heads), int(num_splits)))
+                                                       int(q_dtype), int(num_q_heads),
+                                                       int(num_splits)))
 
 
 def paged_attn_decode(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, num_q_heads: int,

@@ -4,6 +4,8 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -57,6 +59,31 @@ int cu_count() {
   }
   return cache[dev];
 }
+
+}  // namespace
+
+namespace pkv {
+int resident_blocks(const void* kernel, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lk(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  const int r = per_cu * n;
+  cache[key] = r;
+  return r;
+}
+}  // namespace pkv
+
+namespace {
 
 int check_cache(const pkv_cache_t* c, pkv::CacheArgs& out) {
   if (!c) return fail(PKV_EINVAL, "cache is NULL");
@@ -118,51 +145,80 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 struct DecodePlan {
+  bool mfma;       // matrix-core kernels (else the vector-ALU kernel)
+  bool auto_mode;  // matrix-core balanced schedule
+  int waves;       // auto: workgroups launched
   int chunk, max_splits;
-  size_t ws_o_bytes, ws_bytes;
+  size_t off_lse, off_o, off_desc, ws_bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-// Page-aligned partitions of the keys.  A fixed N splits max_context_len into N equal
-// page-aligned parts; the automatic choice aims at a few work items per compute unit
-// (estimated from max_context_len, the only length the host knows), never cutting
-// below 256 keys, and stays a single partition when that already gives enough work.
+constexpr int kMinShareBlocks = 4;  // auto schedule: at least 4 x 32 tokens per wave
+
+// Partition plan of one decode call.
+//  * Matrix-core path (bf16 / FP8 caches, bf16 queries, pages >= 8 tokens):
+//    num_splits == 0 spreads all (sequence, kv head, 32-token block) work evenly over
+//    the waves that fit on the device at once; num_splits == N > 0 cuts every
+//    sequence into page-aligned partitions of ceil(max_context_len / N) tokens
+//    (rounded up to a page and to 32 tokens), one wave each.
+//  * Vector-ALU path: N > 0 as above (page-aligned); 0 aims at a few work items per
+//    compute unit, never below 256 keys per partition.
+// Workspace: partial log-sum-exps and normalised partial outputs (fp32), plus one
+// 16-byte descriptor per wave for the balanced schedule.
 DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
-                       int num_splits) {
+                       int q_dtype, int num_splits) {
   const int P = c.page_size;
   const int64_t maxL = s.max_context_len;
+  const int G = num_q_heads / c.num_kv_heads;
+  DecodePlan p{};
+  p.mfma = pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, P);
+  if (p.mfma && num_splits == 0) {
+    p.auto_mode = true;
+    p.waves = std::max(1, pkv::mfma_auto_waves(c.dtype, c.head_dim, G, P));
+    p.chunk = 0;
+    p.max_splits = 0;
+    const size_t recs = size_t(2) * p.waves;
+    p.off_desc = 0;
+    p.off_lse = align256(size_t(p.waves) * 16);
+    p.off_o = p.off_lse + align256(recs * G * sizeof(float));
+    p.ws_bytes = p.off_o + align256(recs * G * c.head_dim * sizeof(float));
+    return p;
+  }
   int64_t chunk;
   if (num_splits > 0) {
-    chunk = cdiv(cdiv(maxL, num_splits), P) * P;
+    const int64_t gran = p.mfma ? std::max(P, 32) : P;
+    chunk = cdiv(cdiv(maxL, num_splits), gran) * gran;
+    chunk = std::min<int64_t>(chunk, cdiv(maxL, gran) * gran);
   } else {
     const int64_t target = 8LL * cu_count();
     const int64_t est = cdiv(int64_t(s.num_seqs) * c.num_kv_heads * maxL, target);
     chunk = cdiv(std::max<int64_t>(est, std::max(256, P)), P) * P;
+    chunk = std::min<int64_t>(std::max<int64_t>(chunk, P), cdiv(maxL, P) * P);
   }
-  chunk = std::min<int64_t>(std::max<int64_t>(chunk, P), cdiv(maxL, P) * P);
-  DecodePlan p;
   p.chunk = int(chunk);
   p.max_splits = int(cdiv(maxL, chunk));
   if (p.max_splits <= 1) {
     p.max_splits = 1;
-    p.ws_o_bytes = p.ws_bytes = 0;
-  } else {
-    const size_t slots = size_t(s.num_seqs) * num_q_heads * p.max_splits;
-    p.ws_o_bytes = align256(slots * c.head_dim * sizeof(float));
-    p.ws_bytes = p.ws_o_bytes + align256(slots * sizeof(float));
+    p.ws_bytes = 0;
+    return p;
   }
+  const size_t slots = size_t(s.num_seqs) * num_q_heads * p.max_splits;  // (row, q head, split)
+  p.off_lse = 0;
+  p.off_o = align256(slots * sizeof(float));
+  p.ws_bytes = p.off_o + align256(slots * c.head_dim * sizeof(float));
   return p;
 }
 
-int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads) {
+int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads, bool decode) {
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
     return fail(PKV_EINVAL, "q_dtype must be PKV_F32 or PKV_BF16 (got %d)", q_dtype);
   if (num_q_heads < 1 || num_q_heads % c.num_kv_heads)
     return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, c.num_kv_heads);
   const int G = num_q_heads / c.num_kv_heads;
-  if (!pkv::valu_supported(c.dtype, q_dtype, c.head_dim, G))
+  if (!pkv::valu_supported(c.dtype, q_dtype, c.head_dim, G) &&
+      !(decode && pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size)))
     return fail(PKV_EUNSUPPORTED, "no kernel for cache dtype %d, q dtype %d, head_dim %d, group %d",
                 c.dtype, q_dtype, c.head_dim, G);
   return check_fp8_scales(c, false);
@@ -193,12 +249,13 @@ int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_ne
 }
 
 size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
-                                        int32_t num_q_heads, int32_t num_splits) {
+                                        int32_t q_dtype, int32_t num_q_heads, int32_t num_splits) {
   pkv::CacheArgs c;
   pkv::SeqArgs s;
   if (check_cache(cache, c) != PKV_OK || check_seqs(seqs, c, s) != PKV_OK) return 0;
-  if (s.num_seqs == 0 || num_q_heads < 1 || num_splits < 0) return 0;
-  return plan_decode(c, s, num_q_heads, num_splits).ws_bytes;
+  if (s.num_seqs == 0 || num_splits < 0) return 0;
+  if (check_attn(c, q_dtype, num_q_heads, true) != PKV_OK) return 0;
+  return plan_decode(c, s, num_q_heads, q_dtype, num_splits).ws_bytes;
 }
 
 int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
@@ -209,18 +266,19 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
   int st;
   if ((st = check_cache(cache, a.cache)) != PKV_OK) return st;
   if ((st = check_seqs(seqs, a.cache, a.seqs)) != PKV_OK) return st;
-  if ((st = check_attn(a.cache, q_dtype, num_q_heads)) != PKV_OK) return st;
+  if ((st = check_attn(a.cache, q_dtype, num_q_heads, true)) != PKV_OK) return st;
   if (num_splits < 0) return fail(PKV_EINVAL, "num_splits must be >= 0");
   if (a.seqs.num_seqs == 0) return ok();
   if (!q || !out) return fail(PKV_EINVAL, "q and out must not be NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
-  const DecodePlan p = plan_decode(a.cache, a.seqs, num_q_heads, num_splits);
+  const DecodePlan p = plan_decode(a.cache, a.seqs, num_q_heads, q_dtype, num_splits);
   if (p.ws_bytes) {
     if (!workspace || workspace_bytes < p.ws_bytes)
       return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
                   workspace ? workspace_bytes : size_t(0));
     if (!aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
   }
+  char* ws = static_cast<char*>(workspace);
   a.q = q;
   a.q_dtype = q_dtype;
   a.num_q_heads = num_q_heads;
@@ -229,9 +287,17 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
   a.lse_out = lse_out;
   a.chunk = p.chunk;
   a.max_splits = p.max_splits;
-  a.ws_o = p.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-  a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + p.ws_o_bytes) : nullptr;
-  return launch_status(pkv::launch_valu_decode(a, static_cast<hipStream_t>(stream)), "paged_attn_decode");
+  a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
+  a.ws_o = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.mfma) {
+    a.num_waves = p.waves;
+    a.min_share = kMinShareBlocks;
+    a.ws_desc = p.auto_mode ? reinterpret_cast<int4*>(ws + p.off_desc) : nullptr;
+    pkv::MfmaPlan mp{p.auto_mode, p.waves};
+    return launch_status(pkv::launch_mfma_decode(a, mp, hs), "paged_attn_decode");
+  }
+  return launch_status(pkv::launch_valu_decode(a, hs), "paged_attn_decode");
 }
 
 int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
@@ -245,7 +311,7 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
   int st;
   if ((st = check_cache(cache, a.cache)) != PKV_OK) return st;
   if ((st = check_seqs(seqs, a.cache, a.seqs)) != PKV_OK) return st;
-  if ((st = check_attn(a.cache, q_dtype, num_q_heads)) != PKV_OK) return st;
+  if ((st = check_attn(a.cache, q_dtype, num_q_heads, false)) != PKV_OK) return st;
   if (total_q < 0 || max_q_len < 0) return fail(PKV_EINVAL, "total_q and max_q_len must be >= 0");
   if (a.seqs.num_seqs == 0 || total_q == 0) return ok();
   if (!q || !out || !cu_q_lens) return fail(PKV_EINVAL, "q, out and cu_q_lens must not be NULL");

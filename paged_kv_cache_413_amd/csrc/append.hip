@@ -7,7 +7,9 @@
 // read and write ("TensorRT-LLM", 技术原理, 调度策略嵌入).
 //
 // One workgroup per packed row; each thread moves 8 consecutive elements of one
-// (K|V, head) row, so a bf16 row of 8 heads x 128 dims is 256 threads x 16 bytes.
+// (K|V, head) row, so a bf16 row of 8 heads x 128 dims is 256 threads x 16 bytes read.
+// K rows are stored with one vector store; V goes to the dim-major V tile, one
+// element per dim.
 #include "device_common.h"
 #include "internal.h"
 
@@ -37,40 +39,71 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
   const int D = c.head_dim, H = c.num_kv_heads;
   const int vec_per_head = D / 8;
   const int vec_per_row = H * vec_per_head;
+  const int log2P = c.log2_page;
   for (int i = threadIdx.x; i < 2 * vec_per_row; i += blockDim.x) {
     const int kv = i >= vec_per_row;
     const int j = i - kv * vec_per_row;
     const int h = j / vec_per_head;
     const int e0 = (j - h * vec_per_head) * 8;
     const int64_t src = (int64_t(row) * H + h) * D + e0;
-    const int64_t dst = row_offset(bt, pos, c.log2_page, kv, h, H, D) + e0;
     const void* in = kv ? v_new : k_new;
+    // K rows are contiguous in the tile (one vector store); V is dim-major, so the
+    // eight elements go to eight slots of consecutive dims, P elements apart.
+    const int64_t dst = elem_offset(bt, pos, log2P, kv, h, H, D, e0);
+    const int64_t step = kv ? (int64_t(1) << log2P) : 1;
     if constexpr (KV == DT_F32) {
       const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(in) + src);
-      float4* d4 = reinterpret_cast<float4*>(static_cast<float*>(c.pool) + dst);
-      d4[0] = s4[0];
-      d4[1] = s4[1];
+      float* pool = static_cast<float*>(c.pool);
+      if (!kv) {
+        float4* d4 = reinterpret_cast<float4*>(pool + dst);
+        d4[0] = s4[0];
+        d4[1] = s4[1];
+      } else {
+        const float4 a = s4[0], b = s4[1];
+        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pool[dst + e * step] = x[e];
+      }
     } else if constexpr (KV == DT_BF16) {
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(c.pool) + dst) =
-          *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + src);
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + src);
+      uint16_t* pool = static_cast<uint16_t*>(c.pool);
+      if (!kv) {
+        *reinterpret_cast<uint4*>(pool + dst) = w;
+      } else {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pool[dst + e * step] = uint16_t(ws[e >> 1] >> ((e & 1) * 16));
+      }
     } else {  // bf16 in, E4M3 out
       const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + src);
       const float inv = (kv ? c.v_inv_scale : c.k_inv_scale)[h];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t out[2] = {0u, 0u};
+      uint32_t code[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // one IEEE float32 multiply per element, then one rounding into E4M3
-        const uint32_t lo = f32_to_e4m3(__fmul_rn(bf16_lo(ws[e]), inv));
-        const uint32_t hi = f32_to_e4m3(__fmul_rn(bf16_hi(ws[e]), inv));
-        out[e >> 1] |= (lo | (hi << 8)) << ((e & 1) * 16);
+        code[2 * e] = f32_to_e4m3(__fmul_rn(bf16_lo(ws[e]), inv));
+        code[2 * e + 1] = f32_to_e4m3(__fmul_rn(bf16_hi(ws[e]), inv));
       }
-      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(c.pool) + dst) = make_uint2(out[0], out[1]);
+      uint8_t* pool = static_cast<uint8_t*>(c.pool);
+      if (!kv) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo |= code[e] << (8 * e);
+          hi |= code[4 + e] << (8 * e);
+        }
+        *reinterpret_cast<uint2*>(pool + dst) = make_uint2(lo, hi);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pool[dst + e * step] = uint8_t(code[e]);
+      }
     }
   }
 }
 
-// Gather: one workgroup per (4-token block, sequence), 16-byte copies of whole rows.
+// Gather: one workgroup per (4-token block, sequence); each thread writes 16 bytes of
+// one logical (token, K|V, head) row, read from the row (K) or column (V) of the tile.
 __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs sq,
                                                            uint8_t* __restrict__ k_out,
                                                            uint8_t* __restrict__ v_out) {
@@ -80,6 +113,7 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs 
   const int row_bytes = c.head_dim * eb;
   const int vec_per_head = row_bytes / 16;
   const int vec_per_tok = c.num_kv_heads * vec_per_head;
+  const int per16 = 16 / eb;  // elements per 16 bytes
   const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
   const uint8_t* pool = static_cast<const uint8_t*>(c.pool);
   const int t0 = blockIdx.x * 4;
@@ -91,10 +125,17 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs 
     const int kv = rem >= vec_per_tok;
     const int j = rem - kv * vec_per_tok;
     const int h = j / vec_per_head;
-    const int v16 = j - h * vec_per_head;
-    const int64_t src = row_offset(bt, t, c.log2_page, kv, h, c.num_kv_heads, c.head_dim) * eb + v16 * 16;
-    const int64_t dst = ((int64_t(s) * sq.max_context_len + t) * c.num_kv_heads + h) * row_bytes + v16 * 16;
-    *reinterpret_cast<uint4*>((kv ? v_out : k_out) + dst) = *reinterpret_cast<const uint4*>(pool + src);
+    const int d0 = (j - h * vec_per_head) * per16;
+    const int64_t dst = ((int64_t(s) * sq.max_context_len + t) * c.num_kv_heads + h) * row_bytes + d0 * eb;
+    uint8_t* out = (kv ? v_out : k_out) + dst;
+    const int64_t src = elem_offset(bt, t, c.log2_page, kv, h, c.num_kv_heads, c.head_dim, d0) * eb;
+    if (!kv) {
+      *reinterpret_cast<uint4*>(out) = *reinterpret_cast<const uint4*>(pool + src);
+    } else {
+      const int64_t stride = int64_t(eb) << c.log2_page;
+      for (int e = 0; e < per16; ++e)
+        for (int b = 0; b < eb; ++b) out[e * eb + b] = pool[src + e * stride + b];
+    }
   }
 }
 

@@ -2,8 +2,7 @@
 //
 // It serves every supported combination (f32 / bf16 / FP8 caches, f32 or bf16
 // queries, head_dim 64 or 128, GQA groups 1..8), both decode rows and causal
-// prefill rows.  The MFMA kernel (attn_mfma.hip) takes over the shapes where the
-// matrix cores pay off.
+// prefill rows.
 //
 // What it computes (per query row and head):  z_t = scale * q . K_t over the keys
 // the row may see, softmax over z, output = sum_t softmax_t V_t.  A decode step
@@ -16,9 +15,10 @@
 // merge_kernel.  A row whose keys fit one partition writes its output directly.
 //
 // Inside a workgroup (4 waves): a token row of D elements is read by D/8 lanes, 8
-// elements each (16-byte loads for bf16), so one wave covers 64/(D/8) consecutive
-// tokens per step -- for bf16 D=128 that is 4 rows = 1 KiB contiguous per load
-// instruction.  The q.K partial dot products are summed across the D/8 lanes with
+// elements each (16-byte loads of the token-major K tile; the dim-major V tile is read
+// element by element), so one wave covers 64/(D/8) consecutive tokens per step.  This
+// kernel is the general fallback (f32 caches and queries, pages shorter than 8
+// tokens, prefill rows); the matrix-core kernel serves the bandwidth-critical shapes.  The q.K partial dot products are summed across the D/8 lanes with
 // cross-lane shuffles; each group of D/8 lanes runs its own online softmax over its
 // tokens, and the groups are merged once at the end (shuffles, then LDS across waves).
 #include "device_common.h"
@@ -46,6 +46,25 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t off
     fp8x2_to_f32(w.x, true, x[2], x[3]);
     fp8x2_to_f32(w.y, false, x[4], x[5]);
     fp8x2_to_f32(w.y, true, x[6], x[7]);
+  }
+}
+
+// Eight elements `stride` apart: eight consecutive dims of one token in the dim-major
+// V tile.
+template <int KV>
+__device__ __forceinline__ void load8_strided(const void* __restrict__ base, int64_t off,
+                                              int64_t stride, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (KV == DT_F32) {
+      x[e] = static_cast<const float*>(base)[off + e * stride];
+    } else if constexpr (KV == DT_BF16) {
+      x[e] = __uint_as_float(uint32_t(static_cast<const uint16_t*>(base)[off + e * stride]) << 16);
+    } else {
+      float a, b;
+      fp8x2_to_f32(uint32_t(static_cast<const uint8_t*>(base)[off + e * stride]), false, a, b);
+      x[e] = a;
+    }
   }
 }
 
@@ -113,7 +132,6 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   const int r = lane / LPR, c = lane % LPR;
   const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
   const void* pool = a.cache.pool;
-  const int64_t v_delta = int64_t(Hkv) * a.cache.page_size * D;  // K tile -> V tile
   const float qscale = a.sm_scale * kLog2e;
   float kscale = 1.f, vscale = 1.f;
   if constexpr (KV == DT_FP8) {
@@ -141,10 +159,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   for (int tb = t0 + w * RPW; tb < t1; tb += kWaves * RPW) {
     const int t = tb + r;
     if (t < t1) {
-      const int64_t koff = row_offset(bt, t, a.cache.log2_page, 0, g, Hkv, D) + c * 8;
+      const int64_t koff = elem_offset(bt, t, a.cache.log2_page, 0, g, Hkv, D, c * 8);
+      const int64_t voff = elem_offset(bt, t, a.cache.log2_page, 1, g, Hkv, D, c * 8);
       float k[8], v[8];
       load8<KV>(pool, koff, k);
-      load8<KV>(pool, koff + v_delta, v);
+      load8_strided<KV>(pool, voff, a.cache.page_size, v);
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {

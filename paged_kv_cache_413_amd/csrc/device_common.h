@@ -4,8 +4,12 @@
 // Page addressing ("NVIDIA TensorRT-LLM详解：架构、KV Cache、调度与部署实践", §9: a
 // request's logical blocks map to physical blocks through its block table):
 // logical token t of a sequence lives in physical page block_table[t >> log2P] at
-// slot t & (P - 1); the pool is [page][K|V][kv_head][slot][dim], so one (page, K|V,
-// kv_head) tile is P*D contiguous elements and one token row is D contiguous ones.
+// slot t & (P - 1).  The pool is [page][K|V][kv_head][tile], one tile of P*D elements
+// per (page, K|V, kv_head):
+//   K tile: token-major [slot][dim]  (one token's row is D contiguous elements)
+//   V tile: dim-major   [dim][slot]  (one dim of P consecutive tokens is contiguous)
+// The V tile is stored transposed so that the P.V product reads, per lane, eight
+// consecutive tokens of one dim -- the layout the matrix cores take -- straight from HBM.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,12 +28,15 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int kv, int head, i
   return ((int64_t(page) * 2 + kv) * num_kv_heads + head) * int64_t(page_size) * head_dim;
 }
 
-// Element offset of token t's row (kv, head) for the sequence whose table row is bt.
-__device__ __forceinline__ int64_t row_offset(const int32_t* __restrict__ bt, int t, int log2P,
-                                              int kv, int head, int num_kv_heads, int head_dim) {
+// Element offset of element (t, d) of kv head `head` of the sequence whose table row
+// is bt; kv = 0 (K) or 1 (V).
+__device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, int t, int log2P,
+                                               int kv, int head, int num_kv_heads, int head_dim,
+                                               int d) {
   const int32_t page = bt[t >> log2P];
   const int slot = t & ((1 << log2P) - 1);
-  return tile_offset(page, kv, head, num_kv_heads, 1 << log2P, head_dim) + int64_t(slot) * head_dim;
+  const int64_t tile = tile_offset(page, kv, head, num_kv_heads, 1 << log2P, head_dim);
+  return kv == 0 ? tile + int64_t(slot) * head_dim + d : tile + (int64_t(d) << log2P) + slot;
 }
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }

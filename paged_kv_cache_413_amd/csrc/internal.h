@@ -42,14 +42,32 @@ struct AttnArgs {
   int total_q, max_q_len;    // prefill only
   // split-KV (decode): partitions of `chunk` tokens (a multiple of the page size)
   int chunk, max_splits;
-  float* ws_o;    // [rows][Hq][max_splits][D] normalised partial outputs
-  float* ws_lse;  // [rows][Hq][max_splits] partial log-sum-exp
+  float* ws_o;    // normalised partial outputs (layout per kernel family)
+  float* ws_lse;  // partial log-sum-exp
+  // matrix-core decode, auto schedule: resident waves, minimum blocks per wave and the
+  // per-wave descriptor of its first (sequence, kv head) segment
+  int num_waves, min_share;
+  int4* ws_desc;
 };
+
+// Occupancy-derived number of workgroups of `block` threads of `kernel` that fit on
+// the current device at once (cached per device and kernel).
+int resident_blocks(const void* kernel, int block);
 
 // General vector-ALU kernels (attn_valu.hip): every supported combination.
 bool valu_supported(int kv_dtype, int q_dtype, int head_dim, int group);
 hipError_t launch_valu_decode(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_valu_prefill(const AttnArgs& a, hipStream_t stream);
+
+// Matrix-core decode kernels (attn_mfma.hip): bf16 / FP8 caches with bf16 queries,
+// page sizes >= 8, groups of up to 16 query heads per kv head.
+struct MfmaPlan {
+  bool auto_mode;  // true: balanced shares over `waves`; false: fixed partitions
+  int waves;
+};
+bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, int page_size);
+int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size);
+hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t stream);
 
 // Debug gather
 hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,

@@ -114,7 +114,8 @@ class DeviceBatch:
         self.seqs_dec = B.make_seqs(self.bt_dec, self.ctx_dec, dec_max)
         self.out_dec = torch.empty((self.ndec, Hq, D), dtype=qdt, device=dev)
         self.lse_dec = torch.empty((self.ndec, Hq), dtype=torch.float32, device=dev)
-        ws = B.paged_attn_decode_workspace_size(self.cache, self.seqs_dec, Hq, self.num_splits) if self.ndec else 0
+        ws = (B.paged_attn_decode_workspace_size(self.cache, self.seqs_dec, self.q_code, Hq, self.num_splits)
+              if self.ndec else 0)
         self.ws_dec = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.ws_dec_bytes = ws
         self._step_ready = True

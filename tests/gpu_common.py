@@ -29,3 +29,13 @@ def assert_lse_close(got, ref, kv_dtype, what=""):
     err = float(np.abs(got - ref).max()) if got.size else 0.0
     assert err <= LSE_ATOL[kv_dtype], f"{what}: lse error {err:.3e}"
     return err
+
+
+def pool_token_major(bits):
+    """The library's pool [page][K|V][kv_head][tile] (K tiles token-major [P][D], V tiles
+    dim-major [D][P]) rearranged with both tiles token-major, the oracle's layout.  A
+    pure re-indexing of the stored elements, for byte-exact comparison."""
+    N, _, H, P, D = bits.shape
+    out = bits.copy()
+    out[:, 1] = bits[:, 1].reshape(N, H, D, P).swapaxes(-1, -2)
+    return out

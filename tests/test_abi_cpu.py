@@ -88,7 +88,7 @@ def test_bad_attention_args_rejected(lib):
     assert _decode(lib, c, s, splits=-1) == B.PKV_EINVAL
     # a fixed split count needs a workspace
     assert _decode(lib, c, s, splits=4) == B.PKV_EWORKSPACE
-    need = lib.paged_attn_decode_workspace_size(ctypes.byref(c), ctypes.byref(s), 4, 4)
+    need = lib.paged_attn_decode_workspace_size(ctypes.byref(c), ctypes.byref(s), B.PKV_BF16, 4, 4)
     assert need > 0
     assert _decode(lib, c, s, splits=4, ws=0x100000, wsb=need - 1) == B.PKV_EWORKSPACE
     # FP8 caches need their scales

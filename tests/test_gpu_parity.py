@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, assert_lse_close
+from tests.gpu_common import assert_close, assert_lse_close, pool_token_major
 from tests.oracle_state import oracle_outputs, oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,7 @@ def test_append_is_bit_exact(gpu_lib, name):
     db.append_step()
     torch.cuda.synchronize()
     ref = oracle_pool(wl)
-    got = db.pool_bits()
+    got = pool_token_major(db.pool_bits())
     assert got.shape == ref.shape
     assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \
         f"{int((got.view(np.uint8) != ref.view(np.uint8)).sum())} bytes differ"
@@ -167,7 +167,40 @@ def test_one_hot_probe_checks_gather_through_attention(gpu_lib):
     db.decode_step()
     torch.cuda.synchronize()
     out = db.out_dec.float().cpu()
+    Hkv, P, D = wl.num_kv_heads, wl.page_size, wl.head_dim
+    v_tiles = pool[:, 1].reshape(-1, Hkv, D, P)     # V tiles are dim-major
     for s, t in enumerate(target):
         page, slot = int(wl.block_tables[s][t // wl.page_size]), t % wl.page_size
-        want = pool[page, 1, :, slot, :].float().repeat_interleave(wl.group_size, dim=0)
+        want = v_tiles[page, :, :, slot].float().repeat_interleave(wl.group_size, dim=0)
         assert torch.equal(out[s], want), s
+
+
+MFMA_EDGES = [
+    # (page_size, lens, num_q_heads, num_kv_heads, head_dim, num_splits)
+    (8, [1, 7, 8, 9, 31, 32, 33, 100], 32, 8, 128, 0),
+    (16, [1, 15, 16, 17, 63, 64, 65, 200], 8, 8, 64, 0),
+    (32, [1, 31, 32, 33, 95, 300], 16, 8, 128, 0),
+    (64, [1, 2, 63, 64, 65, 129, 1000], 64, 8, 128, 0),
+    (128, [1, 127, 128, 129, 700], 32, 2, 64, 0),
+    (64, [1, 63, 64, 65, 700, 2100], 32, 8, 128, 3),
+    (16, [5, 40, 333], 16, 1, 128, 4),
+]
+
+
+@pytest.mark.parametrize("P,lens,hq,hkv,D,ns", MFMA_EDGES)
+def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
+    """The matrix-core decode kernels on ragged lengths around page and 32-token
+    block edges, pages of 8..128 tokens, groups of 1..16 query heads per kv head,
+    head_dim 64 and 128, balanced and fixed partitions."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(2, lens=lens, page_size=P, num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                        num_splits=ns)
+    print(f"[case] mfma edge P={P} lens={lens} Hq={hq} Hkv={hkv} D={D} splits={ns}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, lse, _, _ = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(dec, ref[0], "bf16", f"P={P}")
+    assert_lse_close(lse, ref[1], "bf16", f"P={P}")

@@ -350,16 +350,22 @@ def _pool_for(pps, shared_pages=0):
 
 def _cfg2(**o):
     """Llama-3-8B-shaped decode, bf16: 64 sequences, lengths U[512,4096], 32/8 heads,
-    D=128, page 64, pool 1.25x the pages needed."""
-    S = o.get("num_seqs", 64)
-    lo, hi = o.get("len_range", (512, 4096))
-    L = _uniform_lens(2, S, lo, hi)
-    P = 64
+    D=128, page 64, pool 1.25x the pages needed.  Overrides for small test variants:
+    num_seqs, len_range or explicit lens, page_size, num_q_heads, num_kv_heads,
+    head_dim, num_splits."""
+    if "lens" in o:
+        L = np.array(o["lens"], np.int32)
+    else:
+        S = o.get("num_seqs", 64)
+        lo, hi = o.get("len_range", (512, 4096))
+        L = _uniform_lens(2, S, lo, hi)
+    P = o.get("page_size", 64)
     pps = _cdiv(L, P)
     npages = _pool_for(pps)
     bt = _assign_pages(2, pps, npages)
-    return Workload("llama3_8b_decode_bf16", 2, 32, 8, 128, P, "bf16", "bf16", npages, L,
-                    np.ones_like(L), bt, num_splits=o.get("num_splits", 0))
+    return Workload("llama3_8b_decode_bf16", 2, o.get("num_q_heads", 32), o.get("num_kv_heads", 8),
+                    o.get("head_dim", 128), P, "bf16", "bf16", npages, L, np.ones_like(L), bt,
+                    num_splits=o.get("num_splits", 0))
 
 
 def _cfg3(**o):
