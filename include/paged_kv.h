@@ -61,9 +61,11 @@ typedef enum {
  *         second axis is K, 1 is V.  A page holds the K and V of page_size
  *         consecutive tokens of one sequence.  16-byte aligned.
  *           K tile: token-major [page_size][head_dim] (a token's row is contiguous)
- *           V tile: dim-major   [head_dim][page_size] (a dim's tokens are contiguous)
+ *           V tile: [page_size / S][head_dim][S] with S = min(page_size, 32): dim-major
+ *                   inside sub-blocks of S slots (a dim's S tokens are contiguous)
  *         V is stored transposed so that the probability-times-V product reads
- *         consecutive tokens of one dim, the operand layout of the matrix cores.
+ *         consecutive tokens of one dim, the operand layout of the matrix cores,
+ *         and one 32-token block's V is one contiguous run.
  *   page_size: power of two, >= 2.     head_dim: 64 or 128.
  *   k_scale / v_scale: FP8 only, [num_kv_heads] float32 dequantization
  *         multipliers (value = decoded code * scale); NULL for F32/BF16 caches.
@@ -147,7 +149,9 @@ size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs
  *   lse_out: NULL or [num_seqs][num_q_heads] float32, natural-log sum of exp of
  *         the scaled logits.
  *   workspace: device buffer of at least paged_attn_decode_workspace_size()
- *         bytes, 256-byte aligned (NULL allowed when that size is 0).
+ *         bytes, 256-byte aligned (NULL allowed when that size is 0); its contents
+ *         need no initialisation.  Calls that run at the same time must not share
+ *         a workspace.
  * Results depend only on logical positions: permuting physical pages (and the
  * tables with them) gives bit-identical output. */
 int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,

@@ -149,7 +149,7 @@ struct DecodePlan {
   bool auto_mode;  // matrix-core balanced schedule
   int waves;       // auto: workgroups launched
   int chunk, max_splits;
-  size_t off_lse, off_o, off_desc, ws_bytes;
+  size_t off_desc, off_lse, off_o, ws_bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -164,7 +164,7 @@ constexpr int kMinShareBlocks = 4;  // auto schedule: at least 4 x 32 tokens per
 //    (rounded up to a page and to 32 tokens), one wave each.
 //  * Vector-ALU path: N > 0 as above (page-aligned); 0 aims at a few work items per
 //    compute unit, never below 256 keys per partition.
-// Workspace: partial log-sum-exps and normalised partial outputs (fp32), plus one
+// Workspace: partial log-sum-exps and normalised partial outputs (fp32), after one
 // 16-byte descriptor per wave for the balanced schedule.
 DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
                        int q_dtype, int num_splits) {
@@ -178,7 +178,7 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
     p.waves = std::max(1, pkv::mfma_auto_waves(c.dtype, c.head_dim, G, P));
     p.chunk = 0;
     p.max_splits = 0;
-    const size_t recs = size_t(2) * p.waves;
+    const size_t recs = size_t(2) * p.waves;  // up to two cut segments per wave
     p.off_desc = 0;
     p.off_lse = align256(size_t(p.waves) * 16);
     p.off_o = p.off_lse + align256(recs * G * sizeof(float));
@@ -204,6 +204,7 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
     return p;
   }
   const size_t slots = size_t(s.num_seqs) * num_q_heads * p.max_splits;  // (row, q head, split)
+  p.off_desc = 0;
   p.off_lse = 0;
   p.off_o = align256(slots * sizeof(float));
   p.ws_bytes = p.off_o + align256(slots * c.head_dim * sizeof(float));

@@ -47,10 +47,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
     const int e0 = (j - h * vec_per_head) * 8;
     const int64_t src = (int64_t(row) * H + h) * D + e0;
     const void* in = kv ? v_new : k_new;
-    // K rows are contiguous in the tile (one vector store); V is dim-major, so the
-    // eight elements go to eight slots of consecutive dims, P elements apart.
+    // K rows are contiguous in the tile (one vector store); V is dim-major inside its
+    // sub-block, so the eight elements go to eight consecutive dims, one sub-block
+    // length apart.
     const int64_t dst = elem_offset(bt, pos, log2P, kv, h, H, D, e0);
-    const int64_t step = kv ? (int64_t(1) << log2P) : 1;
+    const int64_t step = kv ? (int64_t(1) << v_sub_log2(log2P)) : 1;
     if constexpr (KV == DT_F32) {
       const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(in) + src);
       float* pool = static_cast<float*>(c.pool);
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs 
     if (!kv) {
       *reinterpret_cast<uint4*>(out) = *reinterpret_cast<const uint4*>(pool + src);
     } else {
-      const int64_t stride = int64_t(eb) << c.log2_page;
+      const int64_t stride = int64_t(eb) << v_sub_log2(c.log2_page);
       for (int e = 0; e < per16; ++e)
         for (int b = 0; b < eb; ++b) out[e * eb + b] = pool[src + e * stride + b];
     }

@@ -13,8 +13,9 @@
 //   O        [16 heads x D]     += P [16 x 32 tok] . V [32 x D] -> D/16 MFMAs
 // Every operand comes straight from HBM in the register layout the MFMA wants:
 //   K tile of a page is token-major [P][D]: lane (m, c) loads 8 dims of one token row;
-//   V tile of a page is dim-major   [D][P]: lane (n, c) loads 8 consecutive tokens of
-//   one dim -- so no LDS transpose sits on the hot path.
+//   V tile of a page is dim-major inside 32-slot sub-blocks [P/32][D][32]: lane (n, c)
+//   loads 8 consecutive tokens of one dim, and the 16 dims of one load are one
+//   contiguous kilobyte -- so no LDS transpose sits on the hot path.
 // The two K sub-tiles use the row orders 8(m/4) + m%4 and 8(m/4) + 4 + m%4, which puts
 // the scores of tokens 8c .. 8c+7 of head n into lane (n, c) -- exactly the P operand
 // of the second product, so scores never leave their lanes.  The row max of the
@@ -24,9 +25,13 @@
 // Schedule: "auto" spreads the flattened (sequence, kv head, block) space evenly over
 // the resident waves (each wave a contiguous run of blocks, possibly spanning several
 // sequences); a range that covers a whole (sequence, kv head) writes the output
-// directly, a cut one writes a normalised partial and its log-sum-exp, and the merge
-// kernel combines the partials exactly.  "fixed" gives each page-aligned partition of
-// a fixed size its own wave, as in a conventional split-KV decode.
+// directly, a cut one writes a normalised partial and its log-sum-exp, and a small
+// merge kernel combines the pieces exactly (log-sum-exp weights).  "fixed" gives each
+// page-aligned partition of a fixed size its own wave, as in a conventional split-KV
+// decode, with the same merge.  (Merging inside the decode kernel, by the last wave
+// to finish a piece, needs agent-scope release/acquire fences; on this chip those
+// write back and invalidate a whole L2 per piece, which costs far more than the
+// second launch.)
 #include "device_common.h"
 #include "internal.h"
 
@@ -40,6 +45,19 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BT = 32;      // tokens per block
 constexpr int LOG2_BT = 5;
+
+// Cache-policy bits of the K/V buffer loads (0 = default; the data is read once).
+#ifndef PKV_KV_LOAD_AUX
+#define PKV_KV_LOAD_AUX 0
+#endif
+// Waves per SIMD the decode kernels are compiled for (register budget 512 / this).
+#ifndef PKV_DECODE_WAVES_PER_EU
+#define PKV_DECODE_WAVES_PER_EU 2
+#endif
+// Blocks whose loads are in flight while one is folded, plus one (2 or 3 buffers).
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 2
+#endif
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -82,14 +100,14 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff
   Frag8 f;
   if constexpr (KV == DT_BF16) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PKV_KV_LOAD_AUX));
     f.w[0] = v[0];
     f.w[1] = v[1];
     f.w[2] = v[2];
     f.w[3] = v[3];
   } else {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PKV_KV_LOAD_AUX));
     f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
     f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
     f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
@@ -110,50 +128,74 @@ struct Block {
   bf16x8 v[D / 16];               // V: D/16 tiles of 16 dims x 32 tokens
 };
 
-// Per-lane byte offsets inside a tile, fixed for the whole range: lane (m, c) reads
-// K row ra(m) (sub-tile a; +4 rows for b) at dims 8c.., and V dim m (+16 per V tile)
-// at tokens 8c..  (relative to the block's first slot).
+// Per-lane byte offsets, fixed for the whole range: lane (m, c) reads K row ra(m)
+// (sub-tile a; +4 rows for b) at dims 8c.. (relative to the block's first slot), and
+// V dim m (+16 per V tile) at tokens 8c.. of the block's 32-slot V sub-block.
 struct LaneOffsets {
   uint32_t k, v;
 };
 
 template <int KV, int D>
-__device__ __forceinline__ LaneOffsets lane_offsets(int log2P, int lane) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int m = lane & 15, c = lane >> 4;
   const int ra = 8 * (m >> 2) + (m & 3);
-  return {uint32_t((ra * D + 8 * c) * esz), uint32_t(((m << log2P) + 8 * c) * esz)};
+  return {uint32_t((ra * D + 8 * c) * esz), uint32_t((m * BT + 8 * c) * esz)};
+}
+
+// 64 consecutive block-table entries of one sequence, one per lane: the page of a
+// block is read from a register (readlane), so no table load sits between one
+// block's loads and the next.  `base` is the logical page of lane 0.
+struct PageWindow {
+  int32_t ids;
+  int base;
+};
+
+// Load the window starting at logical page `base` of a table row with `npages`
+// valid entries (entries past them read as 0 and are never used).
+__device__ __forceinline__ void load_window(PageWindow& w, const int32_t* __restrict__ bt, int base,
+                                            int npages, int lane) {
+  w.base = base;
+  w.ids = base + lane < npages ? bt[base + lane] : 0;
+}
+
+// Page of logical page p, refilling the window when p has left it (at most once per
+// 64 pages).
+__device__ __forceinline__ int32_t page_of(PageWindow& w, const int32_t* __restrict__ bt, int p,
+                                           int npages, int lane) {
+  if (p - w.base >= 64) load_window(w, bt, p, npages, lane);
+  return __builtin_amdgcn_readlane(w.ids, p - w.base);
 }
 
 // Issue the loads of the block starting at token t (a multiple of 32) of the sequence
 // whose table row is bt.  With pages of >= 32 tokens the block lies in one page, whose
-// id is loaded once per wave (a scalar load) and every address is that page's tile
-// base (uniform) plus the lane's fixed offset.  Shorter pages (SMALLP) take the page
-// of each lane's own tokens, and skip tokens at or past L (the sequence length): their
-// page may not exist.
+// id comes from the page window, and every address is that page's tile base
+// (uniform) plus the lane's fixed offset.  Shorter pages (SMALLP) take the page of
+// each lane's own tokens from the table, and skip tokens at or past L (the sequence
+// length): their page may not exist.
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__ pool,
-                                           const int32_t* __restrict__ bt, int t, int L,
-                                           int log2P, int64_t kv_stride_b, int64_t head_off_b,
+                                           const int32_t* __restrict__ bt, PageWindow& win, int t,
+                                           int L, int log2P, int64_t kv_stride_b, int64_t head_off_b,
                                            LaneOffsets lo, int lane) {
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int P = 1 << log2P;
   if constexpr (!SMALLP) {
-    const int32_t page = __builtin_amdgcn_readfirstlane(bt[t >> log2P]);
+    const int32_t page = page_of(win, bt, t >> log2P, (L + P - 1) >> log2P, lane);
     const uint32_t slot0 = uint32_t(t & (P - 1));
     const uint32_t tile_bytes = uint32_t(P) * D * esz;
     const char* K = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
     const auto rk = tile_rsrc(K, tile_bytes);
     const auto rv = tile_rsrc(K + kv_stride_b, tile_bytes);
-    const uint32_t ks = slot0 * D * esz, vs = slot0 * esz;
+    const uint32_t ks = slot0 * D * esz, vs = slot0 * D * esz;  // V: sub-block slot0/32
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       b.ka[j] = bload8<KV>(rk, lo.k + 32 * j * esz, ks);
       b.kb[j] = bload8<KV>(rk, lo.k + (4 * D + 32 * j) * esz, ks);
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)  // scalar offset per V tile: keeps one lane offset
-      b.v[dt] = bload8<KV>(rv, lo.v, __builtin_amdgcn_readfirstlane(vs + uint32_t(16 * dt * esz) * P));
+    for (int dt = 0; dt < D / 16; ++dt)  // 16 dims x 32 tokens: one contiguous run
+      b.v[dt] = bload8<KV>(rv, lo.v, __builtin_amdgcn_readfirstlane(vs + uint32_t(16 * BT * dt * esz)));
   } else {
     const int m = lane & 15, c = lane >> 4;
     const int ra = 8 * (m >> 2) + (m & 3);
@@ -274,31 +316,71 @@ __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16
 }
 
 // Blocks [b0, b1) of one (sequence, kv head), t_end = last token + 1 of the range.
-// Two register buffers: the loads of block i+1 are in flight while block i is folded.
-// Inside the loop every prefetch is unconditional, so each fold waits only for its
-// own block's loads (a partial vmcnt), never for the prefetch just issued; the last
-// one or two blocks are peeled.
+// PKV_DECODE_DEPTH register buffers rotate: while block i is folded the loads of the
+// next DEPTH-1 blocks are in flight.  Inside the loop every prefetch is
+// unconditional, so each fold waits only for its own block's loads (a partial
+// vmcnt), never for prefetches issued after them; the last blocks are peeled.
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                           int b0, int b1, int t_end, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  const LaneOffsets lo = lane_offsets<KV, D>(log2P, lane);
+  const LaneOffsets lo = lane_offsets<KV, D>(lane);
+  PageWindow win;
+  if constexpr (!SMALLP) load_window(win, bt, (b0 << LOG2_BT) >> log2P, (L + (1 << log2P) - 1) >> log2P, lane);
+  auto ld = [&](Block<D>& b, int blk) {
+    load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
+  };
+  auto fold = [&](Block<D>& b, int blk) { fold_block<D>(st, b, qf, qk_scale, blk << LOG2_BT, t_end, lane); };
   Block<D> x, y;
-  load_block<KV, D, SMALLP>(x, pool, bt, b0 << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
+  ld(x, b0);
   int blk = b0;
-  for (; blk + 2 < b1; blk += 2) {
-    load_block<KV, D, SMALLP>(y, pool, bt, (blk + 1) << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
-    fold_block<D>(st, x, qf, qk_scale, blk << LOG2_BT, t_end, lane);
-    load_block<KV, D, SMALLP>(x, pool, bt, (blk + 2) << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
-    fold_block<D>(st, y, qf, qk_scale, (blk + 1) << LOG2_BT, t_end, lane);
-  }
-  if (blk + 1 < b1) {
-    load_block<KV, D, SMALLP>(y, pool, bt, (blk + 1) << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
-    fold_block<D>(st, x, qf, qk_scale, blk << LOG2_BT, t_end, lane);
-    fold_block<D>(st, y, qf, qk_scale, (blk + 1) << LOG2_BT, t_end, lane);
+  if constexpr (PKV_DECODE_DEPTH == 2) {
+    for (; blk + 2 < b1; blk += 2) {
+      ld(y, blk + 1);
+      fold(x, blk);
+      ld(x, blk + 2);
+      fold(y, blk + 1);
+    }
+    if (blk + 1 < b1) {
+      ld(y, blk + 1);
+      fold(x, blk);
+      fold(y, blk + 1);
+    } else {
+      fold(x, blk);
+    }
   } else {
-    fold_block<D>(st, x, qf, qk_scale, blk << LOG2_BT, t_end, lane);
+    Block<D> z;
+    if (b1 - b0 == 1) {
+      fold(x, blk);
+      return;
+    }
+    ld(y, b0 + 1);
+    for (; blk + 4 < b1; blk += 3) {
+      ld(z, blk + 2);
+      fold(x, blk);
+      ld(x, blk + 3);
+      fold(y, blk + 1);
+      ld(y, blk + 4);
+      fold(z, blk + 2);
+    }
+    const int r = b1 - blk;  // 2..4 blocks left; x and y hold blk, blk+1
+    if (r == 2) {
+      fold(x, blk);
+      fold(y, blk + 1);
+    } else if (r == 3) {
+      ld(z, blk + 2);
+      fold(x, blk);
+      fold(y, blk + 1);
+      fold(z, blk + 2);
+    } else {
+      ld(z, blk + 2);
+      fold(x, blk);
+      ld(x, blk + 3);
+      fold(y, blk + 1);
+      fold(z, blk + 2);
+      fold(x, blk + 3);
+    }
   }
 }
 
@@ -322,17 +404,107 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restr
   }
 }
 
-// Finish a range: reduce the running sum over the four lane groups of each head,
-// normalise, and write either the final output (bf16) and log-sum-exp of query row
-// `row`, or a partial record r: ws_o[r][G][D] (normalised) and ws_lse[r][G].
+// Merge the n partial records of one (query row, kv head) -- record i is rec(i) --
+// into the final output and log-sum-exp: LSE_h = log sum_i exp(lse_ih),
+// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  One 256-thread workgroup: every thread
+// owns float4 chunks of the G x D record (one head each) and a stride of records,
+// and keeps a running (max, sum of weights, weighted sum) over them, so the loads
+// of different records are independent and in flight together; the record-parallel
+// states are then combined in LDS.
+constexpr int kMergeThreads = 256;
+
+template <int D, int G, typename RecFn>
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g, int n, RecFn rec) {
+  constexpr int NT = kMergeThreads;
+  constexpr int C = G * D / 4;                  // float4 chunks per record
+  constexpr int CC = C < NT ? C : NT;           // chunk lanes
+  constexpr int RP = NT / CC;                   // record-parallel factor
+  constexpr int CPT = (C + NT - 1) / NT;        // chunks per thread
+  __shared__ float4 s_acc[RP][CC * CPT];
+  __shared__ float s_m[RP][CC * CPT], s_w[RP][CC * CPT];
+  const int t = threadIdx.x;
+  const int cl = t % CC, rp = t / CC;
+  float4 acc[CPT];
+  float m[CPT], w[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    m[k] = -INFINITY;
+    w[k] = 0.f;
+  }
+#pragma unroll 4
+  for (int i = rp; i < n; i += RP) {
+    const int64_t r = rec(i);
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int e = (cl + k * CC) * 4;
+      if (e < G * D) {
+        const float x = a.ws_lse[r * G + e / D];
+        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + r * (G * D) + e);
+        const float mn = fmaxf(m[k], x);
+        const float sa = __expf(m[k] - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
+        acc[k].x = acc[k].x * sa + o.x * sb;
+        acc[k].y = acc[k].y * sa + o.y * sb;
+        acc[k].z = acc[k].z * sa + o.z * sb;
+        acc[k].w = acc[k].w * sa + o.w * sb;
+        w[k] = w[k] * sa + sb;
+        m[k] = mn;
+      }
+    }
+  }
+  if constexpr (RP > 1) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      s_acc[rp][cl + k * CC] = acc[k];
+      s_m[rp][cl + k * CC] = m[k];
+      s_w[rp][cl + k * CC] = w[k];
+    }
+    __syncthreads();
+    if (rp != 0) return;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      for (int q = 1; q < RP; ++q) {
+        const float mo = s_m[q][cl + k * CC];
+        if (mo == -INFINITY) continue;  // that lane had no records
+        const float4 o = s_acc[q][cl + k * CC];
+        const float mn = fmaxf(m[k], mo);
+        const float sa = __expf(m[k] - mn), sb = __expf(mo - mn);
+        acc[k].x = acc[k].x * sa + o.x * sb;
+        acc[k].y = acc[k].y * sa + o.y * sb;
+        acc[k].z = acc[k].z * sa + o.z * sb;
+        acc[k].w = acc[k].w * sa + o.w * sb;
+        w[k] = w[k] * sa + s_w[q][cl + k * CC] * sb;
+        m[k] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int e = (cl + k * CC) * 4;
+    if (e < G * D) {
+      const int h = e / D, d = e % D;
+      const float inv = 1.f / w[k];
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G + h) * D + d;
+      const uint32_t lo = f32_to_bf16(acc[k].x * inv) | (f32_to_bf16(acc[k].y * inv) << 16);
+      const uint32_t hi = f32_to_bf16(acc[k].z * inv) | (f32_to_bf16(acc[k].w * inv) << 16);
+      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+      if (a.lse_out && d == 0) a.lse_out[int64_t(row) * a.num_q_heads + g * G + h] = m[k] + __logf(w[k]);
+    }
+  }
+}
+
+// Finish a range: reduce the running sum over the four lane groups of each head and
+// normalise.  A range that covers its whole (query row, kv head) writes the output
+// (bf16) and log-sum-exp directly; a cut one writes partial record `rec`:
+// ws_o[rec][G][D] (normalised) and ws_lse[rec][G], merged by the merge kernel.
 template <int D, int G>
 __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, int row, int g,
                                        bool complete, int64_t rec, float vscale, int lane) {
-  const int n = lane & 15, c = lane >> 4;
+  const int nn = lane & 15, c = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const float lse = (st.m + __log2f(l)) * kLn2;  // natural log, valid in lanes n < G
+  const float lse = (st.m + __log2f(l)) * kLn2;  // natural log, valid in lanes nn < G
   float inv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) inv[i] = vscale / __shfl(l, 4 * c + i, 64);
@@ -343,24 +515,24 @@ __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, in
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * c + i;
       if (h < G) {
-        uint16_t* o = out + (int64_t(row) * Hq + g * G + h) * D + n;
+        uint16_t* o = out + (int64_t(row) * Hq + g * G + h) * D + nn;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = uint16_t(f32_to_bf16(st.o[dt][i] * inv[i]));
       }
     }
-    if (a.lse_out && c == 0 && n < G) a.lse_out[int64_t(row) * Hq + g * G + n] = lse;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * c + i;
-      if (h < G) {
-        float* o = a.ws_o + (rec * G + h) * D + n;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = st.o[dt][i] * inv[i];
-      }
-    }
-    if (c == 0 && n < G) a.ws_lse[rec * G + n] = lse;
+    if (a.lse_out && c == 0 && nn < G) a.lse_out[int64_t(row) * Hq + g * G + nn] = lse;
+    return;
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * c + i;
+    if (h < G) {
+      float* o = a.ws_o + (rec * G + h) * D + nn;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = st.o[dt][i] * inv[i];
+    }
+  }
+  if (c == 0 && nn < G) a.ws_lse[rec * G + nn] = lse;
 }
 
 template <int KV>
@@ -375,7 +547,7 @@ __device__ __forceinline__ void scales(const AttnArgs& a, int g, float& qk_scale
 
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fixed_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int split = blockIdx.x % a.max_splits;
   const int sg = blockIdx.x / a.max_splits;
@@ -405,6 +577,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // Flattened order: sequence-major, then kv head, then block; segment (s, g) covers
 // [Hkv*cum_s + g*nb_s, +nb_s) with nb_s = ceil(L_s / 32) and cum_s = sum_{s'<s} nb_s'.
 
+// A value every lane holds equally, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -421,7 +600,7 @@ __device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens
   for (int s = lane; s < S; s += 64) sum += (lens[s] + BT - 1) >> LOG2_BT;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  return sum * Hkv;
+  return uniform64(sum * Hkv);
 }
 
 // Sequence whose segments contain flat block f, and its cum (blocks before it).
@@ -436,17 +615,17 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, int S, 
     if (hit) {
       const int first = __builtin_ctzll(hit);
       s_out = base + first;
-      cum_out = run + __shfl(incl - nb, first, 64);
+      cum_out = uniform64(run + __shfl(incl - nb, first, 64));
       return;
     }
-    run += __shfl(incl, 63, 64);
+    run = uniform64(run + __shfl(incl, 63, 64));
   }
   s_out = S;
   cum_out = run;
 }
 
 template <int KV, int D, int G, bool SMALLP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_auto_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int w = blockIdx.x;
   const int S = a.seqs.num_seqs, Hkv = a.cache.num_kv_heads;
@@ -475,8 +654,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const int64_t gs = seg0 + int64_t(g) * nb;            // this segment's first flat block
     const int b0 = int(f - gs);
     const int b1 = int(min(int64_t(nb), fend - gs));
-    if (first && lane == 0)
-      *desc = make_int4(s, g, int(gs - f0), int(gs + nb - f0));  // relative to f0: fits int
+    if (first && lane == 0) {
+      // This wave merges its first segment when that segment started in an earlier
+      // wave (w0) and ends inside this one.  Record slot of w0: 1 unless the segment
+      // is w0's first too.
+      const int64_t w0 = gs / share;
+      const bool merges = gs < f0 && gs + nb <= fend;
+      *desc = make_int4(s, g, int(w0), merges ? (1 | (gs != w0 * share ? 2 : 0)) : 0);
+    }
     float qk_scale, vscale;
     scales<KV>(a, g, qk_scale, vscale);
     bf16x8 qf[D / 32];
@@ -498,66 +683,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
 }
 
-// Merge of one cut segment, done by the wave that finished it: the segment whose
-// first block lies before this wave's share and whose last block lies inside it.
-// Its partials are those of waves w0 .. w (slot 1 of w0 when the segment is not w0's
-// first, slot 0 otherwise).  LSE = log sum_j exp(lse_j); out = sum_j exp(lse_j - LSE) o_j.
+// Merge of one cut (sequence, kv head) segment of the balanced schedule, by the
+// workgroup of the wave that holds its last piece (a wave is the last one of at
+// most one cut segment: its first).  The pieces are in waves w0 .. w; the record of
+// wave v is slot 0, except slot 1 for w0 when the segment is not w0's first.
 template <int D, int G>
-__global__ __launch_bounds__(128) void merge_auto_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_auto_kernel(AttnArgs a) {
   const int w = blockIdx.x;
-  const int4 d = a.ws_desc[w];
-  // nothing to do unless this wave's first segment started in an earlier wave
-  if (d.x < 0 || d.z >= 0) return;
-  const int S = a.seqs.num_seqs, Hkv = a.cache.num_kv_heads;
-  const int64_t T = total_blocks(a.seqs.context_lens, S, Hkv, threadIdx.x & 63);
-  const int64_t share = max(int64_t(a.min_share), (T + a.num_waves - 1) / a.num_waves);
-  const int64_t f0 = int64_t(w) * share;
-  const int64_t gs = f0 + d.z, ge = f0 + d.w;
-  if (ge > f0 + share) return;  // continues into the next wave, which merges it
-  const int64_t w0 = gs / share;
-  const int s = d.x, g = d.y, Hq = a.num_q_heads;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, dd = i % D;
-    float M = -INFINITY;
-    for (int64_t v = w0; v <= w; ++v) {
-      const int64_t r = v * 2 + ((v == w0 && gs != w0 * share) ? 1 : 0);
-      M = fmaxf(M, a.ws_lse[r * G + h]);
-    }
-    float wsum = 0.f, o = 0.f;
-    for (int64_t v = w0; v <= w; ++v) {
-      const int64_t r = v * 2 + ((v == w0 && gs != w0 * share) ? 1 : 0);
-      const float e = __expf(a.ws_lse[r * G + h] - M);
-      wsum += e;
-      o += e * a.ws_o[(r * G + h) * D + dd];
-    }
-    static_cast<uint16_t*>(a.out)[(int64_t(s) * Hq + g * G + h) * D + dd] = uint16_t(f32_to_bf16(o / wsum));
-    if (a.lse_out && dd == 0) a.lse_out[int64_t(s) * Hq + g * G + h] = M + __logf(wsum);
-  }
+  const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
+  if (d.x < 0 || !(d.w & 1)) return;
+  const int64_t w0 = d.z;
+  const bool slot1 = d.w & 2;
+  merge_partials<D, G>(a, d.x, d.y, int(w - w0 + 1),
+                       [w0, slot1](int i) { return (w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0); });
 }
 
 // Merge of the fixed partitions of one (sequence, kv head).
 template <int D, int G>
-__global__ __launch_bounds__(128) void merge_fixed_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) {
   const int sg = blockIdx.x;
   const int Hkv = a.cache.num_kv_heads;
   const int g = sg % Hkv, s = sg / Hkv;
   const int n = (a.seqs.context_lens[s] + a.chunk - 1) / a.chunk;
   if (n <= 1) return;  // written directly
-  const int Hq = a.num_q_heads;
   const int64_t r0 = int64_t(sg) * a.max_splits;
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D, dd = i % D;
-    float M = -INFINITY;
-    for (int j = 0; j < n; ++j) M = fmaxf(M, a.ws_lse[(r0 + j) * G + h]);
-    float wsum = 0.f, o = 0.f;
-    for (int j = 0; j < n; ++j) {
-      const float e = __expf(a.ws_lse[(r0 + j) * G + h] - M);
-      wsum += e;
-      o += e * a.ws_o[((r0 + j) * G + h) * D + dd];
-    }
-    static_cast<uint16_t*>(a.out)[(int64_t(s) * Hq + g * G + h) * D + dd] = uint16_t(f32_to_bf16(o / wsum));
-    if (a.lse_out && dd == 0) a.lse_out[int64_t(s) * Hq + g * G + h] = M + __logf(wsum);
-  }
+  merge_partials<D, G>(a, s, g, n, [r0](int i) { return r0 + i; });
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -568,7 +718,7 @@ hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
     hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP>), dim3(p.waves), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(p.waves), dim3(128), 0, st, a);
+    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(p.waves), dim3(kMergeThreads), 0, st, a);
     return hipGetLastError();
   }
   const int64_t nblk = int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads * a.max_splits;
@@ -576,7 +726,7 @@ hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL((merge_fixed_kernel<D, G>), dim3(unsigned(int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads)),
-                     dim3(128), 0, st, a);
+                     dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 

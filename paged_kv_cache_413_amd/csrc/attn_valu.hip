@@ -49,8 +49,8 @@ __device__ __forceinline__ void load8(const void* __restrict__ base, int64_t off
   }
 }
 
-// Eight elements `stride` apart: eight consecutive dims of one token in the dim-major
-// V tile.
+// Eight elements `stride` apart: eight consecutive dims of one token in the V tile
+// (dim-major inside its sub-block).
 template <int KV>
 __device__ __forceinline__ void load8_strided(const void* __restrict__ base, int64_t off,
                                               int64_t stride, float (&x)[8]) {
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
       const int64_t voff = elem_offset(bt, t, a.cache.log2_page, 1, g, Hkv, D, c * 8);
       float k[8], v[8];
       load8<KV>(pool, koff, k);
-      load8_strided<KV>(pool, voff, a.cache.page_size, v);
+      load8_strided<KV>(pool, voff, int64_t(1) << v_sub_log2(a.cache.log2_page), v);
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {

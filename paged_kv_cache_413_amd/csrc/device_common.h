@@ -7,9 +7,11 @@
 // slot t & (P - 1).  The pool is [page][K|V][kv_head][tile], one tile of P*D elements
 // per (page, K|V, kv_head):
 //   K tile: token-major [slot][dim]  (one token's row is D contiguous elements)
-//   V tile: dim-major   [dim][slot]  (one dim of P consecutive tokens is contiguous)
+//   V tile: [P/S][dim][S], S = min(P, 32): dim-major inside sub-blocks of 32 slots
 // The V tile is stored transposed so that the P.V product reads, per lane, eight
-// consecutive tokens of one dim -- the layout the matrix cores take -- straight from HBM.
+// consecutive tokens of one dim -- the layout the matrix cores take -- straight from
+// HBM; cutting it into 32-slot sub-blocks makes the V of one 32-token block one
+// contiguous run (D x 32 elements).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,6 +30,9 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int kv, int head, i
   return ((int64_t(page) * 2 + kv) * num_kv_heads + head) * int64_t(page_size) * head_dim;
 }
 
+// log2 of the V sub-block length: 32 slots, or the whole page when it is shorter.
+__host__ __device__ __forceinline__ int v_sub_log2(int log2P) { return log2P < 5 ? log2P : 5; }
+
 // Element offset of element (t, d) of kv head `head` of the sequence whose table row
 // is bt; kv = 0 (K) or 1 (V).
 __device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, int t, int log2P,
@@ -36,7 +41,9 @@ __device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, i
   const int32_t page = bt[t >> log2P];
   const int slot = t & ((1 << log2P) - 1);
   const int64_t tile = tile_offset(page, kv, head, num_kv_heads, 1 << log2P, head_dim);
-  return kv == 0 ? tile + int64_t(slot) * head_dim + d : tile + (int64_t(d) << log2P) + slot;
+  if (kv == 0) return tile + int64_t(slot) * head_dim + d;
+  const int ls = v_sub_log2(log2P);
+  return tile + ((int64_t(slot >> ls) * head_dim + d) << ls) + (slot & ((1 << ls) - 1));
 }
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }

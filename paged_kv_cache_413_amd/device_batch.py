@@ -116,7 +116,7 @@ class DeviceBatch:
         self.lse_dec = torch.empty((self.ndec, Hq), dtype=torch.float32, device=dev)
         ws = (B.paged_attn_decode_workspace_size(self.cache, self.seqs_dec, self.q_code, Hq, self.num_splits)
               if self.ndec else 0)
-        self.ws_dec = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.ws_dec = torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)  # counters start at 0
         self.ws_dec_bytes = ws
         self._step_ready = True
 

@@ -31,11 +31,19 @@ def assert_lse_close(got, ref, kv_dtype, what=""):
     return err
 
 
+def v_tiles_token_major(v_bits):
+    """V tiles [N][H][P/S][D][S] (S = min(P, 32), the library's layout, stored in an
+    array shaped [N][H][P][D]) re-indexed token-major [N][H][P][D]."""
+    N, H, P, D = v_bits.shape
+    S = min(P, 32)
+    return v_bits.reshape(N, H, P // S, D, S).swapaxes(-1, -2).reshape(N, H, P, D)
+
+
 def pool_token_major(bits):
     """The library's pool [page][K|V][kv_head][tile] (K tiles token-major [P][D], V tiles
-    dim-major [D][P]) rearranged with both tiles token-major, the oracle's layout.  A
-    pure re-indexing of the stored elements, for byte-exact comparison."""
-    N, _, H, P, D = bits.shape
+    dim-major inside 32-slot sub-blocks) rearranged with both tiles token-major, the
+    oracle's layout.  A pure re-indexing of the stored elements, for byte-exact
+    comparison."""
     out = bits.copy()
-    out[:, 1] = bits[:, 1].reshape(N, H, D, P).swapaxes(-1, -2)
+    out[:, 1] = v_tiles_token_major(bits[:, 1])
     return out

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, assert_lse_close, pool_token_major
+from tests.gpu_common import assert_close, assert_lse_close, pool_token_major, v_tiles_token_major
 from tests.oracle_state import oracle_outputs, oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -167,11 +167,11 @@ def test_one_hot_probe_checks_gather_through_attention(gpu_lib):
     db.decode_step()
     torch.cuda.synchronize()
     out = db.out_dec.float().cpu()
-    Hkv, P, D = wl.num_kv_heads, wl.page_size, wl.head_dim
-    v_tiles = pool[:, 1].reshape(-1, Hkv, D, P)     # V tiles are dim-major
+    # V tiles token-major: [page][head][slot][dim] (bf16 viewed as int16 for NumPy)
+    v_tiles = torch.from_numpy(v_tiles_token_major(pool[:, 1].view(torch.int16).numpy())).view(torch.bfloat16)
     for s, t in enumerate(target):
         page, slot = int(wl.block_tables[s][t // wl.page_size]), t % wl.page_size
-        want = v_tiles[page, :, :, slot].float().repeat_interleave(wl.group_size, dim=0)
+        want = v_tiles[page, :, slot, :].float().repeat_interleave(wl.group_size, dim=0)
         assert torch.equal(out[s], want), s
 
 
