@@ -16,11 +16,12 @@
 //   V tile of a page is dim-major inside 32-slot sub-blocks [P/32][D][32]: lane (n, c)
 //   loads 8 consecutive tokens of one dim, and the 16 dims of one load are one
 //   contiguous kilobyte -- so no LDS transpose sits on the hot path.
-// The two K sub-tiles use the row orders 8(m/4) + m%4 and 8(m/4) + 4 + m%4, which puts
-// the scores of tokens 8c .. 8c+7 of head n into lane (n, c) -- exactly the P operand
-// of the second product, so scores never leave their lanes.  The row max of the
-// online softmax needs two cross-lane steps (lanes 16 and 32 apart); the running sum
-// is kept per lane and reduced once per range.
+// The two K sub-tiles are tokens 0..15 and 16..31 of the block, so the scores of
+// head n land in lane (n, c) for tokens 4c..4c+3 and 16+4c..16+4c+3 -- exactly the P
+// operand of the second product (k index 8c + e), so scores never leave their lanes;
+// the V sub-block stores its slots in that same order.  The row max of the online
+// softmax needs two cross-lane steps (lanes 16 and 32 apart); the running sum is
+// kept per lane and reduced once per range.
 //
 // Schedule: "auto" spreads the flattened (sequence, kv head, block) space evenly over
 // the resident waves (each wave a contiguous run of blocks, possibly spanning several
@@ -116,6 +117,23 @@ __device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return f.v;
 }
 
+// Four consecutive cache elements at byte offset `off`, as bf16 in words 0 and 1.
+template <int KV>
+__device__ __forceinline__ Frag8 load4x2(const char* __restrict__ base, uint32_t off) {
+  Frag8 f;
+  f.q = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (KV == DT_BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(base + off);
+    f.w[0] = w.x;
+    f.w[1] = w.y;
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(base + off);
+    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  }
+  return f;
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   Frag8 f;
   f.q = make_uint4(0u, 0u, 0u, 0u);
@@ -124,13 +142,17 @@ __device__ __forceinline__ bf16x8 zero8() {
 
 template <int D>
 struct Block {
-  bf16x8 ka[D / 32], kb[D / 32];  // the two 16-token K sub-tiles, D/32 dim chunks each
+  bf16x8 ka[D / 32], kb[D / 32];  // K of tokens 0..15 and 16..31, D/32 dim chunks each
   bf16x8 v[D / 16];               // V: D/16 tiles of 16 dims x 32 tokens
 };
 
-// Per-lane byte offsets, fixed for the whole range: lane (m, c) reads K row ra(m)
-// (sub-tile a; +4 rows for b) at dims 8c.. (relative to the block's first slot), and
-// V dim m (+16 per V tile) at tokens 8c.. of the block's 32-slot V sub-block.
+// Token (0..31 within the block) behind element e of lane group c of the P and V
+// operands.
+__device__ __forceinline__ int tok_of(int c, int e) { return e < 4 ? 4 * c + e : 12 + 4 * c + e; }
+
+// Per-lane byte offsets, fixed for the whole range: lane (m, c) reads K row m of the
+// block (sub-tile a; +16 rows for b) at dims 8c.. of a 32-dim chunk, and V dim m
+// (+16 per V tile) at positions 8c.. of the block's 32-slot V sub-block.
 struct LaneOffsets {
   uint32_t k, v;
 };
@@ -139,8 +161,7 @@ template <int KV, int D>
 __device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int m = lane & 15, c = lane >> 4;
-  const int ra = 8 * (m >> 2) + (m & 3);
-  return {uint32_t((ra * D + 8 * c) * esz), uint32_t((m * BT + 8 * c) * esz)};
+  return {uint32_t((m * 32 + 8 * c) * esz), uint32_t((m * BT + 8 * c) * esz)};
 }
 
 // 64 consecutive block-table entries of one sequence, one per lane: the page of a
@@ -187,25 +208,27 @@ __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__
     const char* K = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
     const auto rk = tile_rsrc(K, tile_bytes);
     const auto rv = tile_rsrc(K + kv_stride_b, tile_bytes);
-    const uint32_t ks = slot0 * D * esz, vs = slot0 * D * esz;  // V: sub-block slot0/32
+    const uint32_t ks = slot0 * 32 * esz, vs = slot0 * D * esz;  // V: sub-block slot0/32
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      b.ka[j] = bload8<KV>(rk, lo.k + 32 * j * esz, ks);
-      b.kb[j] = bload8<KV>(rk, lo.k + (4 * D + 32 * j) * esz, ks);
+    for (int j = 0; j < D / 32; ++j) {  // chunk j: 16 rows x 64 B, one contiguous run each
+      const uint32_t kj = __builtin_amdgcn_readfirstlane(ks + uint32_t(j * 32 * esz) * P);
+      b.ka[j] = bload8<KV>(rk, lo.k, kj);
+      b.kb[j] = bload8<KV>(rk, lo.k + 16 * 32 * esz, kj);
     }
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt)  // 16 dims x 32 tokens: one contiguous run
       b.v[dt] = bload8<KV>(rv, lo.v, __builtin_amdgcn_readfirstlane(vs + uint32_t(16 * BT * dt * esz)));
   } else {
+    // pages of 8 or 16 slots: V tiles are [D][P] in natural slot order
     const int m = lane & 15, c = lane >> 4;
-    const int ra = 8 * (m >> 2) + (m & 3);
     const int P1 = P - 1;
-    const int ta = t + ra, tb = ta + 4, tv = t + 8 * c;
+    const int ta = t + m, tb = ta + 16;
     const uint32_t kcol = uint32_t(8 * c * esz);
     if (ta < L) {
       const char* K = pool + int64_t(bt[ta >> log2P]) * 2 * kv_stride_b + head_off_b;
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j) b.ka[j] = load8<KV>(K, uint32_t(((ta & P1) * D + 32 * j) * esz) + kcol);
+      for (int j = 0; j < D / 32; ++j)
+        b.ka[j] = load8<KV>(K, uint32_t(((j << log2P) + (ta & P1)) * 32 * esz) + kcol);
     } else {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) b.ka[j] = zero8();
@@ -213,19 +236,32 @@ __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__
     if (tb < L) {
       const char* K = pool + int64_t(bt[tb >> log2P]) * 2 * kv_stride_b + head_off_b;
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j) b.kb[j] = load8<KV>(K, uint32_t(((tb & P1) * D + 32 * j) * esz) + kcol);
+      for (int j = 0; j < D / 32; ++j)
+        b.kb[j] = load8<KV>(K, uint32_t(((j << log2P) + (tb & P1)) * 32 * esz) + kcol);
     } else {
 #pragma unroll
       for (int j = 0; j < D / 32; ++j) b.kb[j] = zero8();
     }
-    if (tv < L) {
-      const char* V = pool + (int64_t(bt[tv >> log2P]) * 2 + 1) * kv_stride_b + head_off_b;
+    // V: tokens 4c..4c+3 (elements 0..3) and 16+4c..16+4c+3 (elements 4..7), four
+    // consecutive slots of one page each
+    const int t0 = t + 4 * c, t1 = t0 + 16;
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        b.v[dt] = load8<KV>(V, uint32_t((((16 * dt + m) << log2P) + (tv & P1)) * esz));
-    } else {
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) b.v[dt] = zero8();
+    for (int dt = 0; dt < D / 16; ++dt) {
+      Frag8 f;
+      f.q = make_uint4(0u, 0u, 0u, 0u);
+      if (t0 < L) {
+        const char* V = pool + (int64_t(bt[t0 >> log2P]) * 2 + 1) * kv_stride_b + head_off_b;
+        const Frag8 h = load4x2<KV>(V, uint32_t((((16 * dt + m) << log2P) + (t0 & P1)) * esz));
+        f.w[0] = h.w[0];
+        f.w[1] = h.w[1];
+      }
+      if (t1 < L) {
+        const char* V = pool + (int64_t(bt[t1 >> log2P]) * 2 + 1) * kv_stride_b + head_off_b;
+        const Frag8 h = load4x2<KV>(V, uint32_t((((16 * dt + m) << log2P) + (t1 & P1)) * esz));
+        f.w[2] = h.w[0];
+        f.w[3] = h.w[1];
+      }
+      b.v[dt] = f.v;
     }
   }
 }
@@ -267,17 +303,18 @@ __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16
     sc[4 + i] = sb[i] * qk_scale;
   }
   if (t + BT > t_end) {  // wave-uniform: the range's last, partial block
-    const int nvalid = t_end - t - 8 * c;  // tokens of this lane's group still in range
+    const int nvalid = t_end - t;  // tokens of the block still in range
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (e >= nvalid) sc[e] = -INFINITY;
+      if (tok_of(c, e) >= nvalid) sc[e] = -INFINITY;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       Frag8 f;
       f.v = b.v[dt];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t keep = (2 * w < nvalid ? 0x0000ffffu : 0u) | (2 * w + 1 < nvalid ? 0xffff0000u : 0u);
+        const uint32_t keep = (tok_of(c, 2 * w) < nvalid ? 0x0000ffffu : 0u) |
+                              (tok_of(c, 2 * w + 1) < nvalid ? 0xffff0000u : 0u);
         f.w[w] &= keep;
       }
       b.v[dt] = f.v;

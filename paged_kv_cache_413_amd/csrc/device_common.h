@@ -6,12 +6,12 @@
 // logical token t of a sequence lives in physical page block_table[t >> log2P] at
 // slot t & (P - 1).  The pool is [page][K|V][kv_head][tile], one tile of P*D elements
 // per (page, K|V, kv_head):
-//   K tile: token-major [slot][dim]  (one token's row is D contiguous elements)
-//   V tile: [P/S][dim][S], S = min(P, 32): dim-major inside sub-blocks of 32 slots
-// The V tile is stored transposed so that the P.V product reads, per lane, eight
-// consecutive tokens of one dim -- the layout the matrix cores take -- straight from
-// HBM; cutting it into 32-slot sub-blocks makes the V of one 32-token block one
-// contiguous run (D x 32 elements).
+//   K tile: [D/32][P][32]  -- 32-dim column chunks, token-major inside a chunk
+//   V tile: [P/S][D][S], S = min(P, 32) -- dim-major inside sub-blocks of S slots;
+//           in a 32-slot sub-block, slot r sits at position vpos(r) (below)
+// Both are laid out for the matrix-core decode: a wave's load of 16 token rows x 32
+// dims of K, or of 16 dims x 32 tokens of V, is one contiguous run, and the slot
+// order inside a V sub-block is the order in which the score tile leaves the lanes.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,6 +33,12 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int kv, int head, i
 // log2 of the V sub-block length: 32 slots, or the whole page when it is shorter.
 __host__ __device__ __forceinline__ int v_sub_log2(int log2P) { return log2P < 5 ? log2P : 5; }
 
+// Position of slot r (0..31) inside a 32-slot V sub-block: slots 4c..4c+3 go to
+// positions 8c..8c+3 and slots 16+4c..16+4c+3 to 8c+4..8c+7 (c = 0..3).
+__host__ __device__ __forceinline__ int vpos(int r) {
+  return 8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3);
+}
+
 // Element offset of element (t, d) of kv head `head` of the sequence whose table row
 // is bt; kv = 0 (K) or 1 (V).
 __device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, int t, int log2P,
@@ -41,9 +47,10 @@ __device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, i
   const int32_t page = bt[t >> log2P];
   const int slot = t & ((1 << log2P) - 1);
   const int64_t tile = tile_offset(page, kv, head, num_kv_heads, 1 << log2P, head_dim);
-  if (kv == 0) return tile + int64_t(slot) * head_dim + d;
+  if (kv == 0) return tile + ((int64_t(d >> 5) << log2P) + slot) * 32 + (d & 31);
   const int ls = v_sub_log2(log2P);
-  return tile + ((int64_t(slot >> ls) * head_dim + d) << ls) + (slot & ((1 << ls) - 1));
+  const int r = slot & ((1 << ls) - 1);
+  return tile + ((int64_t(slot >> ls) * head_dim + d) << ls) + (ls == 5 ? vpos(r) : r);
 }
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }

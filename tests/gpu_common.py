@@ -31,19 +31,49 @@ def assert_lse_close(got, ref, kv_dtype, what=""):
     return err
 
 
+# Position of slot r inside a 32-slot V sub-block of the library's pool (slots 4c..4c+3
+# at 8c..8c+3, slots 16+4c..16+4c+3 at 8c+4..8c+7).
+VPOS = np.array([8 * ((r & 15) >> 2) + 4 * (r >> 4) + (r & 3) for r in range(32)])
+
+
+def k_tiles_token_major(k_bits):
+    """K tiles [N][H][D/32][P][32] (the library's layout, in an array shaped
+    [N][H][P][D]) re-indexed token-major [N][H][P][D]."""
+    N, H, P, D = k_bits.shape
+    return k_bits.reshape(N, H, D // 32, P, 32).transpose(0, 1, 3, 2, 4).reshape(N, H, P, D)
+
+
 def v_tiles_token_major(v_bits):
-    """V tiles [N][H][P/S][D][S] (S = min(P, 32), the library's layout, stored in an
-    array shaped [N][H][P][D]) re-indexed token-major [N][H][P][D]."""
+    """V tiles [N][H][P/S][D][S] (S = min(P, 32), slots of a 32-slot sub-block at
+    positions VPOS) re-indexed token-major [N][H][P][D]."""
     N, H, P, D = v_bits.shape
     S = min(P, 32)
-    return v_bits.reshape(N, H, P // S, D, S).swapaxes(-1, -2).reshape(N, H, P, D)
+    x = v_bits.reshape(N, H, P // S, D, S)
+    if S == 32:
+        x = x[..., VPOS]
+    return x.swapaxes(-1, -2).reshape(N, H, P, D)
 
 
 def pool_token_major(bits):
-    """The library's pool [page][K|V][kv_head][tile] (K tiles token-major [P][D], V tiles
-    dim-major inside 32-slot sub-blocks) rearranged with both tiles token-major, the
-    oracle's layout.  A pure re-indexing of the stored elements, for byte-exact
-    comparison."""
+    """The library's pool [page][K|V][kv_head][tile] rearranged with both tiles
+    token-major [P][D], the oracle's layout.  A pure re-indexing of the stored
+    elements, for byte-exact comparison."""
     out = bits.copy()
+    out[:, 0] = k_tiles_token_major(bits[:, 0])
     out[:, 1] = v_tiles_token_major(bits[:, 1])
+    return out
+
+
+def pool_from_token_major(tm):
+    """Inverse of pool_token_major."""
+    N, _, H, P, D = tm.shape
+    out = tm.copy()
+    out[:, 0] = tm[:, 0].reshape(N, H, P, D // 32, 32).transpose(0, 1, 3, 2, 4).reshape(N, H, P, D)
+    S = min(P, 32)
+    x = tm[:, 1].reshape(N, H, P // S, S, D).swapaxes(-1, -2)
+    if S == 32:
+        y = np.empty_like(x)
+        y[..., VPOS] = x
+        x = y
+    out[:, 1] = x.reshape(N, H, P, D)
     return out

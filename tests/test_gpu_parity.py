@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import assert_close, assert_lse_close, pool_token_major, v_tiles_token_major
+from tests.gpu_common import assert_close, assert_lse_close, pool_from_token_major, pool_token_major
 from tests.oracle_state import oracle_outputs, oracle_pool
 
 pytestmark = pytest.mark.gpu
@@ -153,25 +153,26 @@ def test_one_hot_probe_checks_gather_through_attention(gpu_lib):
     db.prepare_step()
     db.append_step()
     torch.cuda.synchronize()
-    # overwrite K of one chosen token per sequence through the pool, on the host copy
-    pool = db.pool.cpu()
+    # overwrite K of one chosen token per sequence, on a token-major host copy
+    pool = pool_token_major(db.pool_bits()).view(np.uint16).copy()   # bf16 bits
+    big = np.array([64.0], np.float32).view(np.uint32)[0] >> 16
     target = [7, 130, int(wl.context_lens[2]) - 1]
-    q = torch.zeros_like(db.q_dec)
     for s, t in enumerate(target):
         page, slot = int(wl.block_tables[s][t // wl.page_size]), t % wl.page_size
         pool[page, 0, :, slot, :] = 0
-        pool[page, 0, :, slot, 0] = 64.0
-    db.pool.copy_(pool.to(db.dev))
+        pool[page, 0, :, slot, 0] = big
+    stored = pool_from_token_major(pool)
+    db.pool.copy_(torch.from_numpy(stored.view(np.int16)).view(torch.bfloat16).to(db.dev))
+    q = torch.zeros_like(db.q_dec)
     q[:, :, 0] = 64.0
     db.q_dec.copy_(q)
     db.decode_step()
     torch.cuda.synchronize()
     out = db.out_dec.float().cpu()
-    # V tiles token-major: [page][head][slot][dim] (bf16 viewed as int16 for NumPy)
-    v_tiles = torch.from_numpy(v_tiles_token_major(pool[:, 1].view(torch.int16).numpy())).view(torch.bfloat16)
     for s, t in enumerate(target):
         page, slot = int(wl.block_tables[s][t // wl.page_size]), t % wl.page_size
-        want = v_tiles[page, :, slot, :].float().repeat_interleave(wl.group_size, dim=0)
+        v = torch.from_numpy(pool[page, 1, :, slot, :].astype(np.int16)).view(torch.bfloat16).float()
+        want = v.repeat_interleave(wl.group_size, dim=0)
         assert torch.equal(out[s], want), s
 
 
