@@ -47,3 +47,29 @@ def oracle_outputs(wl, pool):
     dec = oracle.decode(pool, wl.block_tables[npf:], wl.context_lens[npf:], dq, wl.q_dtype,
                         wl.sm_scale, wl.kv_dtype, ks, vs)
     return dec[0], dec[1], pf[0], pf[1]
+
+
+def oracle_sequence(wl, s):
+    """Oracle outputs of sequence s alone, from a compact pool holding only its pages
+    (renumbered 0..n-1; the oracle's result does not depend on physical page ids).
+    Returns (out [C][Hq][D], lse [C][Hq]) float64 for its C = new_lens[s] query rows:
+    decode rows for a decode sequence, the causal chunk for a prefill request."""
+    ks, vs, kinv, vinv = scales(wl)
+    _, poison = workloads.fill_bits(wl.kv_dtype)
+    row = wl.block_tables[s]
+    n_used = int((row >= 0).sum())
+    table = np.full((1, len(row)), -1, np.int32)
+    table[0, :n_used] = np.arange(n_used, dtype=np.int32)
+    pool = oracle.new_pool(n_used, wl.num_kv_heads, wl.page_size, wl.head_dim, wl.kv_dtype,
+                           fill=poison)
+    L, C = int(wl.context_lens[s]), int(wl.new_lens[s])
+    k, v = wl.tokens(s, 0, L)
+    oracle.append(pool, table, np.array([L]), np.array([L]), k, v, wl.in_dtype, wl.kv_dtype,
+                  kinv, vinv)
+    cu = wl.cu(wl.new_lens)
+    q = wl.q_packed()[cu[s]:cu[s + 1]]
+    if s < wl.num_prefill:
+        return oracle.prefill_chunk(pool, table, np.array([L]), np.array([0, C]), q, wl.q_dtype,
+                                    wl.sm_scale, wl.kv_dtype, ks, vs)
+    return oracle.decode(pool, table, np.array([L]), q, wl.q_dtype, wl.sm_scale, wl.kv_dtype,
+                         ks, vs)

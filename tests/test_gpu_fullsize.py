@@ -1,0 +1,50 @@
+"""Parity at the full sizes of the five workloads, in the launch configuration the
+benchmark times (the workloads' own partition settings), on sampled outputs.
+
+Each workload runs on the GPU whole; the oracle then recomputes, one sequence at a
+time, the shortest and the longest decode sequence plus a few seeded random ones,
+and every query row of the prefill requests, and compares them element by element
+at the same tolerances as the small parity tests."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_common import assert_close, assert_lse_close
+from tests.oracle_state import oracle_sequence
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {1: 4, 2: 6, 3: 6, 4: 2, 5: 6}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_size_sampled_rows(gpu_lib, cfg):
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(cfg)
+    print(f"[case] full-size {wl.name} S={wl.num_seqs} tokens={int(wl.context_lens.sum())}", flush=True)
+    wl.prefetch()
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, dec_lse, pf, pf_lse = db.outputs_f64()
+    del db
+    torch.cuda.empty_cache()
+    npf = wl.num_prefill
+    lens = wl.context_lens[npf:]
+    picks = {npf + int(np.argmin(lens)), npf + int(np.argmax(lens))}
+    rng = np.random.default_rng(cfg)
+    while len(picks) < min(SAMPLES[cfg], wl.num_seqs - npf):
+        picks.add(int(rng.integers(npf, wl.num_seqs)))
+    for s in sorted(picks):
+        ref_o, ref_l = oracle_sequence(wl, s)
+        r = s - npf
+        assert_close(dec[r:r + 1], ref_o, wl.kv_dtype, f"{wl.name} seq {s}")
+        assert_lse_close(dec_lse[r:r + 1], ref_l, wl.kv_dtype, f"{wl.name} seq {s}")
+    cu = wl.cu(wl.new_lens)
+    for s in range(npf):
+        ref_o, ref_l = oracle_sequence(wl, s)
+        assert_close(pf[cu[s]:cu[s + 1]], ref_o, wl.kv_dtype, f"{wl.name} prefill {s}")
+        assert_lse_close(pf_lse[cu[s]:cu[s + 1]], ref_l, wl.kv_dtype, f"{wl.name} prefill {s}")
+    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {npf} prefill requests", flush=True)
