@@ -164,13 +164,23 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
  * but the last is a multiple of the block size; §6: context requests are packed
  * first).  Query i of sequence s sits at position context_lens[s] - C_s + i and
  * attends to keys 0 .. that position.
- *   q: packed [total_q][num_q_heads][head_dim] of q_dtype (BF16).
+ *   q: packed [total_q][num_q_heads][head_dim] of q_dtype (F32 or BF16; BF16 with a
+ *         BF16 or FP8 cache and pages of >= 8 tokens runs on the matrix cores).
  *   cu_q_lens: [num_seqs + 1] int32 prefix sums of the chunk lengths C_s, with
  *         C_s <= context_lens[s].
  *   total_q, max_q_len: HOST values (rows of q; an upper bound of C_s).
  *   out: [total_q][num_q_heads][head_dim] of q_dtype; lse_out: NULL or
  *         [total_q][num_q_heads] float32.
- *   workspace: unused by this build (pass NULL, 0). */
+ *   workspace: device buffer of at least paged_attn_prefill_workspace_size() bytes,
+ *         256-byte aligned (NULL allowed when that size is 0); no initialisation
+ *         needed; not shared by calls that run at the same time. */
+/* Workspace bytes paged_attn_prefill_chunk needs for these arguments (0 when none;
+ * also 0 for arguments the call would reject).  total_q and max_q_len are HOST
+ * values as in the call. */
+size_t paged_attn_prefill_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
+                                         int32_t q_dtype, int32_t num_q_heads, int32_t total_q,
+                                         int32_t max_q_len);
+
 int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
                              const void* q, int32_t q_dtype, const int32_t* cu_q_lens,
                              int32_t total_q, int32_t max_q_len, int32_t num_q_heads,

@@ -25,7 +25,8 @@ TORCH_DTYPE = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: t
 DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
 EXPORTS = ("kv_append", "paged_attn_decode_workspace_size", "paged_attn_decode",
-           "paged_attn_prefill_chunk", "paged_kv_debug_gather", "paged_kv_last_error")
+           "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
+           "paged_kv_debug_gather", "paged_kv_last_error")
 
 
 class PkvCache(ctypes.Structure):
@@ -66,6 +67,9 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_decode.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.paged_attn_decode.restype = c_int32
+    lib.paged_attn_prefill_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32,
+                                                      c_int32, c_int32]
+    lib.paged_attn_prefill_workspace_size.restype = c_size_t
     lib.paged_attn_prefill_chunk.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_void_p,
                                              c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p,
                                              c_void_p, c_size_t, c_void_p]
@@ -141,10 +145,19 @@ def paged_attn_decode(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, num_q_hea
                                     _stream(stream)))
 
 
+def paged_attn_prefill_workspace_size(cache: PkvCache, seqs: PkvSeqs, q_dtype: int,
+                                      num_q_heads: int, total_q: int, max_q_len: int) -> int:
+    return int(load().paged_attn_prefill_workspace_size(ctypes.byref(cache), ctypes.byref(seqs),
+                                                        int(q_dtype), int(num_q_heads),
+                                                        int(total_q), int(max_q_len)))
+
+
 def paged_attn_prefill_chunk(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, cu_q_lens,
                              total_q: int, max_q_len: int, num_q_heads: int, sm_scale: float,
-                             out, lse_out=None, workspace=None, workspace_bytes: int = 0,
+                             out, lse_out=None, workspace=None, workspace_bytes: int | None = None,
                              stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().paged_attn_prefill_chunk(ctypes.byref(cache), ctypes.byref(seqs), _ptr(q),
                                            int(q_dtype), _ptr(cu_q_lens), int(total_q),
                                            int(max_q_len), int(num_q_heads), float(sm_scale),

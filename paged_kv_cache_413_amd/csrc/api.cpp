@@ -211,7 +211,40 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
   return p;
 }
 
-int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads, bool decode) {
+// Prefill plan.  Matrix-core path: waves of mfma_prefill_queries_per_wave(G) queries of
+// one (sequence, kv head); when those do not fill the device's resident waves, each
+// wave's key range is cut into equal splits (at most 16, each >= 8 blocks of 32 keys
+// on average), merged afterwards.  Workspace: per (query row, kv head, split) the
+// partial log-sum-exps (G floats) and normalised outputs (G x D floats).
+struct PrefillPlan {
+  bool mfma;
+  int qtiles, splits;
+  size_t off_lse, off_o, ws_bytes;
+};
+
+PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
+                         int q_dtype, int total_q, int max_q_len) {
+  PrefillPlan p{};
+  const int G = num_q_heads / c.num_kv_heads;
+  p.mfma = pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size);
+  if (!p.mfma) return p;
+  const int qw = pkv::mfma_prefill_queries_per_wave(G);
+  p.qtiles = int(cdiv(max_q_len, qw));
+  const int64_t base = int64_t(s.num_seqs) * c.num_kv_heads * p.qtiles;
+  const int64_t resident = std::max(1, pkv::mfma_prefill_waves(c.dtype, c.head_dim));
+  int64_t splits = std::max<int64_t>(1, resident / std::max<int64_t>(base, 1));
+  splits = std::min<int64_t>(splits, 16);
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(s.max_context_len, 32) / 8));
+  p.splits = int(splits);
+  if (p.splits == 1) return p;
+  const size_t recs = size_t(total_q) * c.num_kv_heads * p.splits;
+  p.off_lse = 0;
+  p.off_o = align256(recs * G * sizeof(float));
+  p.ws_bytes = p.off_o + align256(recs * G * c.head_dim * sizeof(float));
+  return p;
+}
+
+int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads, bool /*decode*/) {
   if (q_dtype != PKV_F32 && q_dtype != PKV_BF16)
     return fail(PKV_EINVAL, "q_dtype must be PKV_F32 or PKV_BF16 (got %d)", q_dtype);
   if (num_q_heads < 1 || num_q_heads % c.num_kv_heads)
@@ -219,7 +252,7 @@ int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads, bool decod
                 num_q_heads, c.num_kv_heads);
   const int G = num_q_heads / c.num_kv_heads;
   if (!pkv::valu_supported(c.dtype, q_dtype, c.head_dim, G) &&
-      !(decode && pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size)))
+      !pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size))
     return fail(PKV_EUNSUPPORTED, "no kernel for cache dtype %d, q dtype %d, head_dim %d, group %d",
                 c.dtype, q_dtype, c.head_dim, G);
   return check_fp8_scales(c, false);
@@ -301,13 +334,22 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
   return launch_status(pkv::launch_valu_decode(a, hs), "paged_attn_decode");
 }
 
+size_t paged_attn_prefill_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
+                                         int32_t q_dtype, int32_t num_q_heads, int32_t total_q,
+                                         int32_t max_q_len) {
+  pkv::CacheArgs c;
+  pkv::SeqArgs s;
+  if (check_cache(cache, c) != PKV_OK || check_seqs(seqs, c, s) != PKV_OK) return 0;
+  if (s.num_seqs == 0 || total_q <= 0 || max_q_len <= 0) return 0;
+  if (check_attn(c, q_dtype, num_q_heads, false) != PKV_OK) return 0;
+  return plan_prefill(c, s, num_q_heads, q_dtype, total_q, max_q_len).ws_bytes;
+}
+
 int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
                              int32_t q_dtype, const int32_t* cu_q_lens, int32_t total_q,
                              int32_t max_q_len, int32_t num_q_heads, float sm_scale, void* out,
                              float* lse_out, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   pkv::AttnArgs a{};
   int st;
   if ((st = check_cache(cache, a.cache)) != PKV_OK) return st;
@@ -319,6 +361,13 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(PKV_EINVAL, "q and out must be 16-byte aligned");
   if (max_q_len < 1 || max_q_len > a.seqs.max_context_len)
     return fail(PKV_EINVAL, "max_q_len (%d) must be in [1, max_context_len]", max_q_len);
+  const PrefillPlan p = plan_prefill(a.cache, a.seqs, num_q_heads, q_dtype, total_q, max_q_len);
+  if (p.ws_bytes) {
+    if (!workspace || workspace_bytes < p.ws_bytes)
+      return fail(PKV_EWORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                  workspace ? workspace_bytes : size_t(0));
+    if (!aligned(workspace, 256)) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  }
   a.q = q;
   a.q_dtype = q_dtype;
   a.num_q_heads = num_q_heads;
@@ -328,10 +377,18 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
   a.cu_q_lens = cu_q_lens;
   a.total_q = total_q;
   a.max_q_len = max_q_len;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.mfma) {
+    char* ws = static_cast<char*>(workspace);
+    a.max_splits = p.splits;
+    a.pf_qtiles = p.qtiles;
+    a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
+    a.ws_o = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
+    return launch_status(pkv::launch_mfma_prefill(a, hs), "paged_attn_prefill_chunk");
+  }
   a.chunk = int(cdiv(a.seqs.max_context_len, a.cache.page_size) * a.cache.page_size);
   a.max_splits = 1;
-  return launch_status(pkv::launch_valu_prefill(a, static_cast<hipStream_t>(stream)),
-                       "paged_attn_prefill_chunk");
+  return launch_status(pkv::launch_valu_prefill(a, hs), "paged_attn_prefill_chunk");
 }
 
 int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void* k_out,

@@ -33,501 +33,37 @@
 // to finish a piece, needs agent-scope release/acquire fences; on this chip those
 // write back and invalidate a whole L2 per piece, which costs far more than the
 // second launch.)
-#include "device_common.h"
-#include "internal.h"
+#include "mfma_common.h"
 
 namespace pkv {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int BT = 32;      // tokens per block
-constexpr int LOG2_BT = 5;
-
-// Cache-policy bits of the K/V buffer loads (0 = default; the data is read once).
-#ifndef PKV_KV_LOAD_AUX
-#define PKV_KV_LOAD_AUX 0
-#endif
-// Waves per SIMD the decode kernels are compiled for (register budget 512 / this).
-#ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 2
-#endif
-// Blocks whose loads are in flight while one is folded, plus one (2 or 3 buffers).
-#ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 2
-#endif
-
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-union Frag8 {
-  bf16x8 v;
-  uint32_t w[4];
-  uint4 q;
-};
-
-// Eight consecutive cache elements at byte offset `off` of the wave-uniform address
-// `base`, as bf16.  bf16: a 16-byte load.  FP8 E4M3: an 8-byte load, each code widened
-// exactly (every E4M3 value is a bf16 value).
-template <int KV>
-__device__ __forceinline__ bf16x8 load8(const char* __restrict__ base, uint32_t off) {
-  Frag8 f;
-  if constexpr (KV == DT_BF16) {
-    f.q = *reinterpret_cast<const uint4*>(base + off);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(base + off);
-    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
-    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
-    f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
-    f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
-  }
-  return f.v;
-}
-
-// Buffer descriptor of one tile (wave-uniform, 4 scalar registers): loads address it
-// with the lane's fixed 32-bit offset plus a scalar offset, and anything past the
-// tile's `bytes` reads as zero instead of touching other memory.  Word 3 is the
-// gfx9-family default (32-bit data format, no swizzle).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int(bytes), 0x00020000);
-}
-
-template <int KV>
-__device__ __forceinline__ bf16x8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  Frag8 f;
-  if constexpr (KV == DT_BF16) {
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, PKV_KV_LOAD_AUX));
-    f.w[0] = v[0];
-    f.w[1] = v[1];
-    f.w[2] = v[2];
-    f.w[3] = v[3];
-  } else {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PKV_KV_LOAD_AUX));
-    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
-    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
-    f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
-    f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
-  }
-  return f.v;
-}
-
-// Four consecutive cache elements at byte offset `off`, as bf16 in words 0 and 1.
-template <int KV>
-__device__ __forceinline__ Frag8 load4x2(const char* __restrict__ base, uint32_t off) {
-  Frag8 f;
-  f.q = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (KV == DT_BF16) {
-    const uint2 w = *reinterpret_cast<const uint2*>(base + off);
-    f.w[0] = w.x;
-    f.w[1] = w.y;
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(base + off);
-    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
-  }
-  return f;
-}
-
-__device__ __forceinline__ bf16x8 zero8() {
-  Frag8 f;
-  f.q = make_uint4(0u, 0u, 0u, 0u);
-  return f.v;
-}
-
-template <int D>
-struct Block {
-  bf16x8 ka[D / 32], kb[D / 32];  // K of tokens 0..15 and 16..31, D/32 dim chunks each
-  bf16x8 v[D / 16];               // V: D/16 tiles of 16 dims x 32 tokens
-};
-
-// Token (0..31 within the block) behind element e of lane group c of the P and V
-// operands.
-__device__ __forceinline__ int tok_of(int c, int e) { return e < 4 ? 4 * c + e : 12 + 4 * c + e; }
-
-// Per-lane byte offsets, fixed for the whole range: lane (m, c) reads K row m of the
-// block (sub-tile a; +16 rows for b) at dims 8c.. of a 32-dim chunk, and V dim m
-// (+16 per V tile) at positions 8c.. of the block's 32-slot V sub-block.
-struct LaneOffsets {
-  uint32_t k, v;
-};
-
-template <int KV, int D>
-__device__ __forceinline__ LaneOffsets lane_offsets(int lane) {
-  constexpr int esz = KV == DT_BF16 ? 2 : 1;
-  const int m = lane & 15, c = lane >> 4;
-  return {uint32_t((m * 32 + 8 * c) * esz), uint32_t((m * BT + 8 * c) * esz)};
-}
-
-// 64 consecutive block-table entries of one sequence, one per lane: the page of a
-// block is read from a register (readlane), so no table load sits between one
-// block's loads and the next.  `base` is the logical page of lane 0.
-struct PageWindow {
-  int32_t ids;
-  int base;
-};
-
-// Load the window starting at logical page `base` of a table row with `npages`
-// valid entries (entries past them read as 0 and are never used).
-__device__ __forceinline__ void load_window(PageWindow& w, const int32_t* __restrict__ bt, int base,
-                                            int npages, int lane) {
-  w.base = base;
-  w.ids = base + lane < npages ? bt[base + lane] : 0;
-}
-
-// Page of logical page p, refilling the window when p has left it (at most once per
-// 64 pages).
-__device__ __forceinline__ int32_t page_of(PageWindow& w, const int32_t* __restrict__ bt, int p,
-                                           int npages, int lane) {
-  if (p - w.base >= 64) load_window(w, bt, p, npages, lane);
-  return __builtin_amdgcn_readlane(w.ids, p - w.base);
-}
-
-// Issue the loads of the block starting at token t (a multiple of 32) of the sequence
-// whose table row is bt.  With pages of >= 32 tokens the block lies in one page, whose
-// id comes from the page window, and every address is that page's tile base
-// (uniform) plus the lane's fixed offset.  Shorter pages (SMALLP) take the page of
-// each lane's own tokens from the table, and skip tokens at or past L (the sequence
-// length): their page may not exist.
-template <int KV, int D, bool SMALLP>
-__device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__ pool,
-                                           const int32_t* __restrict__ bt, PageWindow& win, int t,
-                                           int L, int log2P, int64_t kv_stride_b, int64_t head_off_b,
-                                           LaneOffsets lo, int lane) {
-  constexpr int esz = KV == DT_BF16 ? 2 : 1;
-  const int P = 1 << log2P;
-  if constexpr (!SMALLP) {
-    const int32_t page = page_of(win, bt, t >> log2P, (L + P - 1) >> log2P, lane);
-    const uint32_t slot0 = uint32_t(t & (P - 1));
-    const uint32_t tile_bytes = uint32_t(P) * D * esz;
-    const char* K = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
-    const auto rk = tile_rsrc(K, tile_bytes);
-    const auto rv = tile_rsrc(K + kv_stride_b, tile_bytes);
-    const uint32_t ks = slot0 * 32 * esz, vs = slot0 * D * esz;  // V: sub-block slot0/32
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {  // chunk j: 16 rows x 64 B, one contiguous run each
-      const uint32_t kj = __builtin_amdgcn_readfirstlane(ks + uint32_t(j * 32 * esz) * P);
-      b.ka[j] = bload8<KV>(rk, lo.k, kj);
-      b.kb[j] = bload8<KV>(rk, lo.k + 16 * 32 * esz, kj);
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)  // 16 dims x 32 tokens: one contiguous run
-      b.v[dt] = bload8<KV>(rv, lo.v, __builtin_amdgcn_readfirstlane(vs + uint32_t(16 * BT * dt * esz)));
-  } else {
-    // pages of 8 or 16 slots: V tiles are [D][P] in natural slot order
-    const int m = lane & 15, c = lane >> 4;
-    const int P1 = P - 1;
-    const int ta = t + m, tb = ta + 16;
-    const uint32_t kcol = uint32_t(8 * c * esz);
-    if (ta < L) {
-      const char* K = pool + int64_t(bt[ta >> log2P]) * 2 * kv_stride_b + head_off_b;
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j)
-        b.ka[j] = load8<KV>(K, uint32_t(((j << log2P) + (ta & P1)) * 32 * esz) + kcol);
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) b.ka[j] = zero8();
-    }
-    if (tb < L) {
-      const char* K = pool + int64_t(bt[tb >> log2P]) * 2 * kv_stride_b + head_off_b;
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j)
-        b.kb[j] = load8<KV>(K, uint32_t(((j << log2P) + (tb & P1)) * 32 * esz) + kcol);
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 32; ++j) b.kb[j] = zero8();
-    }
-    // V: tokens 4c..4c+3 (elements 0..3) and 16+4c..16+4c+3 (elements 4..7), four
-    // consecutive slots of one page each
-    const int t0 = t + 4 * c, t1 = t0 + 16;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      Frag8 f;
-      f.q = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 < L) {
-        const char* V = pool + (int64_t(bt[t0 >> log2P]) * 2 + 1) * kv_stride_b + head_off_b;
-        const Frag8 h = load4x2<KV>(V, uint32_t((((16 * dt + m) << log2P) + (t0 & P1)) * esz));
-        f.w[0] = h.w[0];
-        f.w[1] = h.w[1];
-      }
-      if (t1 < L) {
-        const char* V = pool + (int64_t(bt[t1 >> log2P]) * 2 + 1) * kv_stride_b + head_off_b;
-        const Frag8 h = load4x2<KV>(V, uint32_t((((16 * dt + m) << log2P) + (t1 & P1)) * esz));
-        f.w[2] = h.w[0];
-        f.w[3] = h.w[1];
-      }
-      b.v[dt] = f.v;
-    }
-  }
-}
-
-// Online-softmax state of one wave: running max m (log2 units, per head lane), the
-// lane's share of the running sum, and the output accumulator O [16 heads x D]
-// (lane (n, c) holds heads 4c..4c+3 of dim 16*dt + n in O[dt]).
-template <int D>
-struct State {
-  float m, l;
-  f32x4 o[D / 16];
-};
-
-template <int D>
-__device__ __forceinline__ void state_init(State<D>& st) {
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-// Fold one block into the state.  t_end: first token past this range; when the
-// block reaches past it (the range's last block) the scores of the excess tokens are
-// masked and their V entries zeroed (their slots may hold anything, NaN included).
+// Fold one block into the state of the G heads (the MFMA rows; unused rows are zero).
+// t_end: first token past this range; when the block reaches past it (the range's
+// last block) the excess tokens' scores are masked and their V entries zeroed.
 template <int D>
 __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16x8 (&qf)[D / 32],
                                            float qk_scale, int t, int t_end, int lane) {
-  const int c = lane >> 4;
-  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    sa = mma(b.ka[j], qf[j], sa);
-    sb = mma(b.kb[j], qf[j], sb);
-  }
   float sc[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = sa[i] * qk_scale;
-    sc[4 + i] = sb[i] * qk_scale;
-  }
+  block_scores<D>(b, qf, qk_scale, sc);
   if (t + BT > t_end) {  // wave-uniform: the range's last, partial block
-    const int nvalid = t_end - t;  // tokens of the block still in range
+    const int c = lane >> 4, nvalid = t_end - t;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (tok_of(c, e) >= nvalid) sc[e] = -INFINITY;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      Frag8 f;
-      f.v = b.v[dt];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t keep = (tok_of(c, 2 * w) < nvalid ? 0x0000ffffu : 0u) |
-                              (tok_of(c, 2 * w + 1) < nvalid ? 0xffff0000u : 0u);
-        f.w[w] &= keep;
-      }
-      b.v[dt] = f.v;
-    }
+    mask_v_tail<D>(b, nvalid, lane);
   }
-  float bm = sc[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  const float mn = fmaxf(st.m, bm);
-  const float alpha = exp2f(st.m - mn);  // 0 on the first block (m = -inf)
-  float p[8], ps = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(sc[e] - mn);
-    ps += p[e];
-  }
-  st.l = st.l * alpha + ps;
-  if (__ballot(mn != st.m)) {  // some head's max moved: rescale O by that head's alpha
-    float al[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * c + i, 64);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.o[dt][i] *= al[i];
-  }
-  st.m = mn;
-  Frag8 pa;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    pa.w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = mma(pa.v, b.v[dt], st.o[dt]);
+  softmax_pv<D>(st, b, sc, lane);
 }
 
 // Blocks [b0, b1) of one (sequence, kv head), t_end = last token + 1 of the range.
-// PKV_DECODE_DEPTH register buffers rotate: while block i is folded the loads of the
-// next DEPTH-1 blocks are in flight.  Inside the loop every prefetch is
-// unconditional, so each fold waits only for its own block's loads (a partial
-// vmcnt), never for prefetches issued after them; the last blocks are peeled.
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                           int b0, int b1, int t_end, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  const LaneOffsets lo = lane_offsets<KV, D>(lane);
-  PageWindow win;
-  if constexpr (!SMALLP) load_window(win, bt, (b0 << LOG2_BT) >> log2P, (L + (1 << log2P) - 1) >> log2P, lane);
-  auto ld = [&](Block<D>& b, int blk) {
-    load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
-  };
-  auto fold = [&](Block<D>& b, int blk) { fold_block<D>(st, b, qf, qk_scale, blk << LOG2_BT, t_end, lane); };
-  Block<D> x, y;
-  ld(x, b0);
-  int blk = b0;
-  if constexpr (PKV_DECODE_DEPTH == 2) {
-    for (; blk + 2 < b1; blk += 2) {
-      ld(y, blk + 1);
-      fold(x, blk);
-      ld(x, blk + 2);
-      fold(y, blk + 1);
-    }
-    if (blk + 1 < b1) {
-      ld(y, blk + 1);
-      fold(x, blk);
-      fold(y, blk + 1);
-    } else {
-      fold(x, blk);
-    }
-  } else {
-    Block<D> z;
-    if (b1 - b0 == 1) {
-      fold(x, blk);
-      return;
-    }
-    ld(y, b0 + 1);
-    for (; blk + 4 < b1; blk += 3) {
-      ld(z, blk + 2);
-      fold(x, blk);
-      ld(x, blk + 3);
-      fold(y, blk + 1);
-      ld(y, blk + 4);
-      fold(z, blk + 2);
-    }
-    const int r = b1 - blk;  // 2..4 blocks left; x and y hold blk, blk+1
-    if (r == 2) {
-      fold(x, blk);
-      fold(y, blk + 1);
-    } else if (r == 3) {
-      ld(z, blk + 2);
-      fold(x, blk);
-      fold(y, blk + 1);
-      fold(z, blk + 2);
-    } else {
-      ld(z, blk + 2);
-      fold(x, blk);
-      ld(x, blk + 3);
-      fold(y, blk + 1);
-      fold(z, blk + 2);
-      fold(x, blk + 3);
-    }
-  }
-}
-
-// Q^T operand of query row `row`, kv head g: lane (n, c) holds dims 32j + 8c .. +7 of
-// query head g*G + n (zero for n >= G).  Queries are bf16.
-template <int D, int G>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restrict__ q, int row,
-                                       int Hq, int g, int lane) {
-  const int n = lane & 15, c = lane >> 4;
-  if (n < G) {
-    const uint16_t* base = static_cast<const uint16_t*>(q) + (int64_t(row) * Hq + g * G + n) * D + 8 * c;
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-      Frag8 f;
-      f.q = *reinterpret_cast<const uint4*>(base + 32 * j);
-      qf[j] = f.v;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) qf[j] = zero8();
-  }
-}
-
-// Merge the n partial records of one (query row, kv head) -- record i is rec(i) --
-// into the final output and log-sum-exp: LSE_h = log sum_i exp(lse_ih),
-// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  One 256-thread workgroup: every thread
-// owns float4 chunks of the G x D record (one head each) and a stride of records,
-// and keeps a running (max, sum of weights, weighted sum) over them, so the loads
-// of different records are independent and in flight together; the record-parallel
-// states are then combined in LDS.
-constexpr int kMergeThreads = 256;
-
-template <int D, int G, typename RecFn>
-__device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g, int n, RecFn rec) {
-  constexpr int NT = kMergeThreads;
-  constexpr int C = G * D / 4;                  // float4 chunks per record
-  constexpr int CC = C < NT ? C : NT;           // chunk lanes
-  constexpr int RP = NT / CC;                   // record-parallel factor
-  constexpr int CPT = (C + NT - 1) / NT;        // chunks per thread
-  __shared__ float4 s_acc[RP][CC * CPT];
-  __shared__ float s_m[RP][CC * CPT], s_w[RP][CC * CPT];
-  const int t = threadIdx.x;
-  const int cl = t % CC, rp = t / CC;
-  float4 acc[CPT];
-  float m[CPT], w[CPT];
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-    m[k] = -INFINITY;
-    w[k] = 0.f;
-  }
-#pragma unroll 4
-  for (int i = rp; i < n; i += RP) {
-    const int64_t r = rec(i);
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int e = (cl + k * CC) * 4;
-      if (e < G * D) {
-        const float x = a.ws_lse[r * G + e / D];
-        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + r * (G * D) + e);
-        const float mn = fmaxf(m[k], x);
-        const float sa = __expf(m[k] - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
-        acc[k].x = acc[k].x * sa + o.x * sb;
-        acc[k].y = acc[k].y * sa + o.y * sb;
-        acc[k].z = acc[k].z * sa + o.z * sb;
-        acc[k].w = acc[k].w * sa + o.w * sb;
-        w[k] = w[k] * sa + sb;
-        m[k] = mn;
-      }
-    }
-  }
-  if constexpr (RP > 1) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      s_acc[rp][cl + k * CC] = acc[k];
-      s_m[rp][cl + k * CC] = m[k];
-      s_w[rp][cl + k * CC] = w[k];
-    }
-    __syncthreads();
-    if (rp != 0) return;
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      for (int q = 1; q < RP; ++q) {
-        const float mo = s_m[q][cl + k * CC];
-        if (mo == -INFINITY) continue;  // that lane had no records
-        const float4 o = s_acc[q][cl + k * CC];
-        const float mn = fmaxf(m[k], mo);
-        const float sa = __expf(m[k] - mn), sb = __expf(mo - mn);
-        acc[k].x = acc[k].x * sa + o.x * sb;
-        acc[k].y = acc[k].y * sa + o.y * sb;
-        acc[k].z = acc[k].z * sa + o.z * sb;
-        acc[k].w = acc[k].w * sa + o.w * sb;
-        w[k] = w[k] * sa + s_w[q][cl + k * CC] * sb;
-        m[k] = mn;
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int e = (cl + k * CC) * 4;
-    if (e < G * D) {
-      const int h = e / D, d = e % D;
-      const float inv = 1.f / w[k];
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G + h) * D + d;
-      const uint32_t lo = f32_to_bf16(acc[k].x * inv) | (f32_to_bf16(acc[k].y * inv) << 16);
-      const uint32_t hi = f32_to_bf16(acc[k].z * inv) | (f32_to_bf16(acc[k].w * inv) << 16);
-      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-      if (a.lse_out && d == 0) a.lse_out[int64_t(row) * a.num_q_heads + g * G + h] = m[k] + __logf(w[k]);
-    }
-  }
+  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane,
+                            [&](Block<D>& b, int t) { fold_block<D>(st, b, qf, qk_scale, t, t_end, lane); });
 }
 
 // Finish a range: reduce the running sum over the four lane groups of each head and
@@ -572,16 +108,6 @@ __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, in
   if (c == 0 && nn < G) a.ws_lse[rec * G + nn] = lse;
 }
 
-template <int KV>
-__device__ __forceinline__ void scales(const AttnArgs& a, int g, float& qk_scale, float& vscale) {
-  qk_scale = a.sm_scale * kLog2e;
-  vscale = 1.f;
-  if constexpr (KV == DT_FP8) {
-    qk_scale *= a.cache.k_scale[g];
-    vscale = a.cache.v_scale[g];
-  }
-}
-
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
@@ -613,13 +139,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_W
 // ---- auto: contiguous equal shares of the flattened block space ------------------------
 // Flattened order: sequence-major, then kv head, then block; segment (s, g) covers
 // [Hkv*cum_s + g*nb_s, +nb_s) with nb_s = ceil(L_s / 32) and cum_s = sum_{s'<s} nb_s'.
-
-// A value every lane holds equally, moved to scalar registers.
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll

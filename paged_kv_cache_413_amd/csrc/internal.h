@@ -48,6 +48,8 @@ struct AttnArgs {
   // per-wave descriptor of its first (sequence, kv head) segment
   int num_waves, min_share;
   int4* ws_desc;
+  // matrix-core prefill: query tiles per (sequence, kv head) (key splits: max_splits)
+  int pf_qtiles;
 };
 
 // Occupancy-derived number of workgroups of `block` threads of `kernel` that fit on
@@ -68,6 +70,11 @@ struct MfmaPlan {
 bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, int page_size);
 int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size);
 hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t stream);
+
+// Matrix-core prefill kernels (prefill_mfma.hip): same support as the decode kernels.
+int mfma_prefill_queries_per_wave(int group);
+int mfma_prefill_waves(int kv_dtype, int head_dim);
+hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t stream);
 
 // Debug gather
 hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,

@@ -104,6 +104,10 @@ class DeviceBatch:
             self.out_pf = torch.empty((self.npf_q, Hq, D), dtype=qdt, device=dev)
             self.lse_pf = torch.empty((self.npf_q, Hq), dtype=torch.float32, device=dev)
             self.max_q = int(wl.new_lens[:npf].max())
+            wsp = B.paged_attn_prefill_workspace_size(self.cache, self.seqs_pf, self.q_code,
+                                                      Hq, self.npf_q, self.max_q)
+            self.ws_pf = torch.empty(max(wsp, 1), dtype=torch.uint8, device=dev)
+            self.ws_pf_bytes = wsp
         # decode sequences: rows [npf, S)
         S = wl.num_seqs
         self.ndec = S - npf
@@ -130,7 +134,8 @@ class DeviceBatch:
         wl = self.wl
         B.paged_attn_prefill_chunk(self.cache, self.seqs_pf, self.q_pf, self.q_code, self.cu_q,
                                    self.npf_q, self.max_q, wl.num_q_heads, float(wl.sm_scale),
-                                   self.out_pf, self.lse_pf, stream=stream)
+                                   self.out_pf, self.lse_pf, self.ws_pf, self.ws_pf_bytes,
+                                   stream=stream)
 
     def decode_step(self, stream=None, num_splits=None):
         if not self.ndec:

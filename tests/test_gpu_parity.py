@@ -205,3 +205,37 @@ def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
     ref = oracle_outputs(wl, oracle_pool(wl))
     assert_close(dec, ref[0], "bf16", f"P={P}")
     assert_lse_close(lse, ref[1], "bf16", f"P={P}")
+
+
+PREFILL_EDGES = [
+    # (page_size, chunks, cached, num_q_heads, num_kv_heads, head_dim)
+    (64, [1, 15, 16, 17], [0, 0, 5, 100], 32, 8, 128),       # first chunks: triangular
+    (64, [70, 64, 3], [190, 0, 4000], 32, 8, 128),
+    (128, [33, 130], [0, 257], 16, 16, 64),                   # G = 1, D = 64
+    (32, [40, 9], [31, 300], 16, 8, 128),                     # G = 2
+    (16, [25, 50], [7, 100], 64, 8, 128),                     # G = 8, pages of 16
+    (8, [20, 3], [13, 60], 32, 2, 64),                        # G = 16, pages of 8
+    (64, [300, 5], [600, 2000], 32, 8, 128),                  # several query waves
+]
+
+
+@pytest.mark.parametrize("P,chunks,cached,hq,hkv,D", PREFILL_EDGES)
+def test_prefill_edge_shapes(gpu_lib, P, chunks, cached, hq, hkv, D):
+    """Causal prefill chunks on the matrix cores: first chunks (no cache, triangular
+    masks), chunks of 1 and around the 16-row tile and 32-key block edges, groups of
+    1..16 query heads, head_dim 64 and 128, pages of 8..128, and enough queries for
+    several waves per (sequence, kv head) and for key splits to be merged."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(3, num_seqs=len(chunks) + 2, num_prefill=len(chunks), prefill_chunk=chunks,
+                        prefill_cached=cached, median=50, clip=(1, 300), page_size=P,
+                        num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
+    print(f"[case] prefill edge P={P} chunks={chunks} cached={cached} Hq={hq} Hkv={hkv} D={D}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, dec_lse, pf, pf_lse = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(pf, ref[2], "bf16", f"prefill P={P}")
+    assert_lse_close(pf_lse, ref[3], "bf16", f"prefill P={P}")
+    assert_close(dec, ref[0], "bf16", f"decode P={P}")

@@ -371,22 +371,26 @@ def _cfg2(**o):
 def _cfg3(**o):
     """Mixed in-flight batch, bf16: 2 chunked-prefill requests (512-token chunk against
     8192 cached tokens) packed first, then 256 decode sequences with lognormal lengths
-    (median 1024, sigma 1.0, clipped to [16,16384]); 32/8 heads, D=128, page 64."""
+    (median 1024, sigma 1.0, clipped to [16,16384]); 32/8 heads, D=128, page 64.
+    Overrides for test variants: num_seqs, num_prefill, prefill_chunk and
+    prefill_cached (scalars or one per prefill request), median, clip, page_size,
+    num_q_heads, num_kv_heads, head_dim, num_splits."""
     S = o.get("num_seqs", 256)
     npf = o.get("num_prefill", 2)
-    C = o.get("prefill_chunk", 512)
-    cached = o.get("prefill_cached", 8192)
+    C = np.broadcast_to(np.asarray(o.get("prefill_chunk", 512), np.int32), (npf,))
+    cached = np.broadcast_to(np.asarray(o.get("prefill_cached", 8192), np.int32), (npf,))
     clip = o.get("clip", (16, 16384))
     med = o.get("median", 1024)
     z = _rng(3, _LENS).standard_normal(S)
     Ld = np.clip(np.rint(np.exp(math.log(med) + 1.0 * z)), clip[0], clip[1]).astype(np.int32)
-    L = np.concatenate([np.full(npf, cached + C, np.int32), Ld])
-    new = np.concatenate([np.full(npf, C, np.int32), np.ones(S, np.int32)])
-    P = 64
+    L = np.concatenate([(cached + C).astype(np.int32), Ld])
+    new = np.concatenate([C.astype(np.int32), np.ones(S, np.int32)])
+    P = o.get("page_size", 64)
     pps = _cdiv(L, P)
     npages = _pool_for(pps)
     bt = _assign_pages(3, pps, npages)
-    return Workload("mixed_inflight_bf16", 3, 32, 8, 128, P, "bf16", "bf16", npages, L, new, bt,
+    return Workload("mixed_inflight_bf16", 3, o.get("num_q_heads", 32), o.get("num_kv_heads", 8),
+                    o.get("head_dim", 128), P, "bf16", "bf16", npages, L, new, bt,
                     num_prefill=npf, num_splits=o.get("num_splits", 0))
 
 
