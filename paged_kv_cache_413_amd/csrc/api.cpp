@@ -211,9 +211,10 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
   return p;
 }
 
-// Prefill plan.  Matrix-core path: waves of mfma_prefill_queries_per_wave(G) queries of
-// one (sequence, kv head); when those do not fill the device's resident waves, each
-// wave's key range is cut into equal splits (at most 16, each >= 8 blocks of 32 keys
+// Prefill plan.  Matrix-core path: work items (a workgroup sharing one K/V stream, or
+// a single wave for pages shorter than 32 tokens) of a fixed number of queries of one
+// (sequence, kv head); when those do not fill the device's resident work items, each
+// item's key range is cut into equal splits (at most 16, each >= 8 blocks of 32 keys
 // on average), merged afterwards.  Workspace: per (query row, kv head, split) the
 // partial log-sum-exps (G floats) and normalised outputs (G x D floats).
 struct PrefillPlan {
@@ -228,10 +229,11 @@ PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num
   const int G = num_q_heads / c.num_kv_heads;
   p.mfma = pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size);
   if (!p.mfma) return p;
-  const int qw = pkv::mfma_prefill_queries_per_wave(G);
+  int qw = 1, resident_items = 1;
+  pkv::mfma_prefill_geometry(c.dtype, c.head_dim, G, c.page_size, &qw, &resident_items);
   p.qtiles = int(cdiv(max_q_len, qw));
   const int64_t base = int64_t(s.num_seqs) * c.num_kv_heads * p.qtiles;
-  const int64_t resident = std::max(1, pkv::mfma_prefill_waves(c.dtype, c.head_dim));
+  const int64_t resident = std::max(1, resident_items);
   int64_t splits = std::max<int64_t>(1, resident / std::max<int64_t>(base, 1));
   splits = std::min<int64_t>(splits, 16);
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(s.max_context_len, 32) / 8));

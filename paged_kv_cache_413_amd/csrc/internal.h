@@ -72,8 +72,10 @@ int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size);
 hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t stream);
 
 // Matrix-core prefill kernels (prefill_mfma.hip): same support as the decode kernels.
-int mfma_prefill_queries_per_wave(int group);
-int mfma_prefill_waves(int kv_dtype, int head_dim);
+// Queries of one (sequence, kv head) per work item and work items resident at once,
+// for the prefill kernel these arguments select.
+void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
+                           int* resident_items);
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t stream);
 
 // Debug gather

@@ -34,6 +34,55 @@ struct PfGeom {
   static constexpr int QW = kPrefillTiles * QPT;     // queries per wave
 };
 
+// Finish the NT row tiles of a wave: rows of the chunk only.  One split: output and
+// log-sum-exp; several: partial record (row, kv head, split) for the merge kernel.
+template <int D, int G, int NT>
+__device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D> (&st)[NT], int q0, int C,
+                                               int cq0, int g, int split, float vscale, int lane) {
+  constexpr int QPT = PfGeom<G>::QPT;
+  const int n = lane & 15, c = lane >> 4;
+  const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    float l = st[r].l;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const float lse = l > 0.f ? (st[r].m + __log2f(l)) * kLn2 : -INFINITY;  // row n
+    float inv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lr = __shfl(l, 4 * c + i, 64);
+      inv[i] = lr > 0.f ? vscale / lr : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // O rows 4c+i of this lane
+      const int R = 4 * c + i;
+      const int qi = q0 + r * QPT + R / G, h = R % G;
+      if (qi >= C) continue;
+      const int64_t row = cq0 + qi;
+      if (nsplit == 1) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + (row * Hq + g * G + h) * D + n;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = uint16_t(f32_to_bf16(st[r].o[dt][i] * inv[i]));
+      } else {
+        const int64_t rec = (row * Hkv + g) * nsplit + split;
+        float* o = a.ws_o + (rec * G + h) * D + n;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = st[r].o[dt][i] * inv[i];
+      }
+    }
+    const int qi = q0 + r * QPT + n / G;
+    if (c == 0 && qi < C) {
+      const int64_t row = cq0 + qi;
+      if (nsplit == 1) {
+        if (a.lse_out) a.lse_out[row * Hq + g * G + n % G] = lse;
+      } else {
+        a.ws_lse[((row * Hkv + g) * nsplit + split) * G + n % G] = lse;
+      }
+    }
+  }
+}
+
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(AttnArgs a) {
   constexpr int NT = kPrefillTiles, QPT = PfGeom<G>::QPT, QW = PfGeom<G>::QW;
@@ -104,46 +153,209 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         });
   }
 
-  // finish every tile: rows of the chunk only
+  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, vscale, lane);
+}
+
+// ---- LDS-shared variant (pages of >= 32 tokens) -----------------------------------------
+// A workgroup of kPfWaves waves (two per SIMD, kPfTiles row tiles each, so that one
+// wave's softmax runs while the other's MFMAs do) shares one K/V stream: every 32-token
+// block is fetched once per workgroup -- each thread loads 64 bytes of it into
+// registers two blocks ahead (two register slots), then writes them into one of
+// two LDS stages -- and each wave reads its MFMA operands from the stage with the
+// same lane offsets as from the tile in HBM.  The stage layout mirrors the block's HBM
+// layout: K as D/32 chunks of [32 tokens][32 dims], then V as [D][32 positions].
+constexpr int kPfWaves = 8;     // two per SIMD: one's softmax overlaps the other's MFMAs
+constexpr int kPfTiles = 2;     // 16-row tiles per wave of the LDS-shared kernel
+
+template <int KV, int D>
+struct PfStage {
+  static constexpr int esz = KV == DT_BF16 ? 2 : 1;
+  static constexpr int KCHUNK = BT * 32 * esz;   // one 32-dim chunk of the block's K
+  static constexpr int KBYTES = D * BT * esz;
+  static constexpr int BYTES = 2 * KBYTES;       // K and V of one block
+  static constexpr int KPIECES = KBYTES / 1024;
+  static constexpr int PIECES = BYTES / 1024;    // 1 KiB pieces, one per wave-wide 16-B load
+  static constexpr int PER_WAVE = (PIECES + kPfWaves - 1) / kPfWaves;
+  static constexpr bool EVEN = PIECES % kPfWaves == 0;  // else waves >= PIECES copy nothing
+};
+
+// Workgroup barrier; LDS writes and reads of this wave are complete before it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Eight cache elements of an operand from LDS, as bf16.
+template <int KV>
+__device__ __forceinline__ bf16x8 lds8(const char* p) {
+  Frag8 f;
+  if constexpr (KV == DT_BF16) {
+    f.q = *reinterpret_cast<const uint4*>(p);
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+    f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+    f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  }
+  return f.v;
+}
+
+template <int KV, int D, int G>
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_lds_kernel(AttnArgs a) {
+  using SL = PfStage<KV, D>;
+  constexpr int NT = kPfTiles, QPT = PfGeom<G>::QPT, QWV = NT * QPT;
+  constexpr int QWG = kPfWaves * QWV;
+  constexpr int esz = SL::esz;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * SL::BYTES];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, c = lane >> 4;
+  const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
+  const int QT = a.pf_qtiles;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  const int grp = xcd + kXcds * (slot / QT), qt = slot % QT;
+  if (grp >= a.seqs.num_seqs * Hkv * nsplit) return;  // whole workgroup
+  const int split = grp % nsplit, sg = grp / nsplit;
+  const int g = sg % Hkv, s = sg / Hkv;
+  const int cq0 = a.cu_q_lens[s], C = a.cu_q_lens[s + 1] - cq0;
+  if (qt * QWG >= C) return;                            // whole workgroup
+  const int L = a.seqs.context_lens[s];
+  const int pos0 = L - C;
+  const int kend = pos0 + min(C, qt * QWG + QWG);       // keys any row of the group sees
+  const int nb = (kend + BT - 1) >> LOG2_BT;
+  const int b0 = int(int64_t(nb) * split / nsplit), b1 = int(int64_t(nb) * (split + 1) / nsplit);
+  const int q0 = qt * QWG + w * QWV;                    // this wave's first query
+  const bool live = q0 < C;
+  const int kend_w = live ? pos0 + min(C, q0 + QWV) : 0;  // keys this wave's rows see
+
+  float qk_scale, vscale;
+  scales<KV>(a, g, qk_scale, vscale);
+  bf16x8 qf[NT][D / 32];
+  int lim[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    float l = st[r].l;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float lse = l > 0.f ? (st[r].m + __log2f(l)) * kLn2 : -INFINITY;  // row n
-    float inv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lr = __shfl(l, 4 * c + i, 64);
-      inv[i] = lr > 0.f ? vscale / lr : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // O rows 4c+i of this lane
-      const int R = 4 * c + i;
-      const int qi = q0 + r * QPT + R / G, h = R % G;
-      if (qi >= C) continue;
-      const int64_t row = cq0 + qi;
-      if (nsplit == 1) {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + (row * Hq + g * G + h) * D + n;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = uint16_t(f32_to_bf16(st[r].o[dt][i] * inv[i]));
-      } else {
-        const int64_t rec = (row * Hkv + g) * nsplit + split;
-        float* o = a.ws_o + (rec * G + h) * D + n;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = st[r].o[dt][i] * inv[i];
-      }
-    }
     const int qi = q0 + r * QPT + n / G;
-    if (c == 0 && qi < C) {
-      const int64_t row = cq0 + qi;
-      if (nsplit == 1) {
-        if (a.lse_out) a.lse_out[row * Hq + g * G + n % G] = lse;
-      } else {
-        a.ws_lse[((row * Hkv + g) * nsplit + split) * G + n % G] = lse;
+    lim[r] = qi < C ? pos0 + qi + 1 : 0;
+    if (qi < C) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t(cq0 + qi) * Hq + g * G + n % G) * D + 8 * c;
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) {
+        Frag8 f;
+        f.q = *reinterpret_cast<const uint4*>(qp + 32 * j);
+        qf[r][j] = f.v;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) qf[r][j] = zero8();
     }
   }
+  const int lim_min = pos0 + q0 + 1;
+  State<D> st[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) state_init(st[r]);
+
+  const int log2P = a.cache.log2_page, P = 1 << log2P;
+  const int64_t tile_b = int64_t(P) * D * esz, kv_stride_b = Hkv * tile_b, head_off_b = g * tile_b;
+  const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
+  const char* pool = static_cast<const char*>(a.cache.pool);
+  // this thread's 16-byte share of each of this wave's PER_WAVE pieces of a block
+  // (the page id is a scalar load: it waits on the scalar counter only, never on the
+  // vector loads of the other register slot still in flight)
+  auto fetch = [&](uint4 (&r)[SL::PER_WAVE], int blk) {
+    const int t = blk << LOG2_BT;
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const int32_t page = ((const_i32_ptr)(uintptr_t)bt)[t >> log2P];
+    const uint32_t slot0 = uint32_t(t & (P - 1));
+    const uint32_t tile_bytes = uint32_t(P) * D * esz;
+    const char* Kt = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
+    const auto rk = tile_rsrc(Kt, tile_bytes);
+    const auto rv = tile_rsrc(Kt + kv_stride_b, tile_bytes);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int k = 0; k < SL::PER_WAVE; ++k) {
+      const int p = w + k * kPfWaves;
+      if (!SL::EVEN && p >= SL::PIECES) break;
+      // K or V piece: decided by k alone when the K pieces split evenly over the waves
+      const bool is_k = SL::KPIECES % kPfWaves == 0 ? k * kPfWaves < SL::KPIECES : p < SL::KPIECES;
+      u32x4 v;
+      if (is_k) {
+        const int off = p * 1024;
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t(off / SL::KCHUNK) * P + slot0) * 32 * esz +
+                                                           uint32_t(off % SL::KCHUNK));
+        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * 16, so, 0));
+      } else {
+        const uint32_t so = __builtin_amdgcn_readfirstlane(slot0 * D * esz + uint32_t(p - SL::KPIECES) * 1024);
+        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16, so, 0));
+      }
+      r[k] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+  auto stash = [&](const uint4 (&r)[SL::PER_WAVE], int stage) {
+    char* dst = smem + stage * SL::BYTES;
+#pragma unroll
+    for (int k = 0; k < SL::PER_WAVE; ++k) {
+      if (!SL::EVEN && w + k * kPfWaves >= SL::PIECES) break;
+      *reinterpret_cast<uint4*>(dst + (w + k * kPfWaves) * 1024 + lane * 16) = r[k];
+    }
+  };
+
+  const int nblk = b1 - b0;
+  const uint32_t lk = uint32_t((n * 32 + 8 * c) * esz);  // lane offset in a K chunk / V tile
+  // Fold block b0+i from stage i%2 (the wave's rows only need blocks below kend_w).
+  auto compute = [&](int i) {
+    const int t = (b0 + i) << LOG2_BT;
+    if (t >= kend_w) return;
+    const char* stg = smem + (i & 1) * SL::BYTES;
+    Block<D> b;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      b.ka[j] = lds8<KV>(stg + j * SL::KCHUNK + lk);
+      b.kb[j] = lds8<KV>(stg + j * SL::KCHUNK + 16 * 32 * esz + lk);
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) b.v[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
+    if (t + BT > L) mask_v_tail<D>(b, L - t, lane);
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      float sc[8];
+      block_scores<D>(b, qf[r], qk_scale, sc);
+      if (t + BT > lim_min) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (t + tok_of(c, e) >= lim[r]) sc[e] = -INFINITY;
+      }
+      softmax_pv<D>(st[r], b, sc, lane);
+    }
+  };
+  // Register slots hold the next blocks: ra the even-numbered, rb the odd-numbered
+  // ones.  At step i, block i+1 goes from its slot into stage (i+1)%2 -- last read
+  // during block i-1, before the previous step's barrier -- and the slot refills with
+  // block i+3 (clamped to the last block: a harmless repeat near the end).  Stash and
+  // refill are unconditional and the slots static, so every wait is for the older
+  // slot's loads only.
+  const int last = b1 - 1;
+  uint4 ra[SL::PER_WAVE], rb[SL::PER_WAVE];
+  if (nblk > 0) {
+    fetch(ra, b0);
+    fetch(rb, min(b0 + 1, last));
+    stash(ra, 0);
+    fetch(ra, min(b0 + 2, last));
+    stage_barrier();
+  }
+  int i = 0;
+  for (; i + 1 < nblk; i += 2) {
+    stash(rb, 1);                      // block i+1 (odd) -> stage 1
+    fetch(rb, min(b0 + i + 3, last));
+    compute(i);
+    stage_barrier();
+    stash(ra, 0);                      // block i+2 (even) -> stage 0
+    fetch(ra, min(b0 + i + 4, last));
+    compute(i + 1);
+    stage_barrier();
+  }
+  if (i < nblk) compute(i);
+  if (!live) return;
+  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, vscale, lane);
 }
 
 // Merge of the key splits of one (query row, kv head).
@@ -159,7 +371,11 @@ template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int groups = a.seqs.num_seqs * a.cache.num_kv_heads * a.max_splits;
   const int64_t grid = int64_t((groups + kXcds - 1) / kXcds) * kXcds * a.pf_qtiles;
-  hipLaunchKernelGGL((prefill_kernel<KV, D, G, SMALLP>), dim3(unsigned(grid)), dim3(64), 0, st, a);
+  if constexpr (SMALLP) {
+    hipLaunchKernelGGL((prefill_kernel<KV, D, G, true>), dim3(unsigned(grid)), dim3(64), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prefill_lds_kernel<KV, D, G>), dim3(unsigned(grid)), dim3(64 * kPfWaves), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(unsigned(int64_t(a.total_q) * a.cache.num_kv_heads)),
@@ -191,15 +407,25 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int mfma_prefill_queries_per_wave(int group) { return kPrefillTiles * (16 / group); }
-
-int mfma_prefill_waves(int kv_dtype, int head_dim) {
-  const void* k = kv_dtype == DT_BF16
-                      ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 64, 4, false>)
-                                        : reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 128, 4, false>))
-                      : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 64, 4, false>)
-                                        : reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 128, 4, false>));
-  return resident_blocks(k, 64);
+void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
+                           int* resident_items) {
+  const bool lds = page_size >= BT;
+  *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : kPrefillTiles);
+  const void* k;
+  if (lds) {
+    k = kv_dtype == DT_BF16
+            ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 64, 4>)
+                              : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 128, 4>))
+            : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 64, 4>)
+                              : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 128, 4>));
+  } else {
+    k = kv_dtype == DT_BF16
+            ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 64, 4, true>)
+                              : reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 128, 4, true>))
+            : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 64, 4, true>)
+                              : reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 128, 4, true>));
+  }
+  *resident_items = resident_blocks(k, lds ? 64 * kPfWaves : 64);
 }
 
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t st) {
