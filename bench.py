@@ -151,6 +151,9 @@ def main():
                     help="override the workload's partition count (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-mb", type=float, default=0.0,
+                    help="only run a plain device-to-device copy of this many MB, --steps times "
+                         "(the known-size reference for the HBM byte counters), then exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -166,6 +169,15 @@ def main():
     from paged_kv_cache_413_amd.device_batch import DeviceBatch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_mb > 0:
+        n = int(args.copy_mb * 1e6) // 16 * 16
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "steps": args.steps}), flush=True)
+        return
     binding.load()  # raises when libpagedkv.so is missing: there is no other path
 
     cfg = WORKLOADS[args.workload]

@@ -45,7 +45,7 @@ template <int D>
 __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16x8 (&qf)[D / 32],
                                            float qk_scale, int t, int t_end, int lane) {
   float sc[8];
-  block_scores<D>(b, qf, qk_scale, sc);
+  block_scores<D>(b, qf, sc);
   if (t + BT > t_end) {  // wave-uniform: the range's last, partial block
     const int c = lane >> 4, nvalid = t_end - t;
 #pragma unroll
@@ -53,7 +53,7 @@ __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16
       if (tok_of(c, e) >= nvalid) sc[e] = -INFINITY;
     mask_v_tail<D>(b, nvalid, lane);
   }
-  softmax_pv<D>(st, b, sc, lane);
+  softmax_pv<D>(st, b, sc, qk_scale, lane);
 }
 
 // Blocks [b0, b1) of one (sequence, kv head), t_end = last token + 1 of the range.
@@ -72,15 +72,19 @@ __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 3
 // ws_o[rec][G][D] (normalised) and ws_lse[rec][G], merged by the merge kernel.
 template <int D, int G>
 __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, int row, int g,
-                                       bool complete, int64_t rec, float vscale, int lane) {
+                                       bool complete, int64_t rec, float qk_scale, float vscale,
+                                       int lane) {
   const int nn = lane & 15, c = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const float lse = (st.m + __log2f(l)) * kLn2;  // natural log, valid in lanes nn < G
+  const float lse = row_lse(st.m, l, qk_scale);  // natural log, valid in lanes nn < G
   float inv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) inv[i] = vscale / __shfl(l, 4 * c + i, 64);
+  for (int i = 0; i < 4; ++i) {
+    const float lr = __shfl(l, 4 * c + i, 64);
+    inv[i] = lr > 0.f ? vscale / lr : 0.f;
+  }
   const int Hq = a.num_q_heads;
   if (complete) {
     uint16_t* out = static_cast<uint16_t*>(a.out);
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_W
   run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt,
                            t0 >> LOG2_BT, (t1 + BT - 1) >> LOG2_BT, t1, L, a.cache.log2_page,
                            Hkv * tile_b, g * tile_b, lane);
-  finish<D, G>(st, a, s, g, nsplit == 1, int64_t(sg) * a.max_splits + split, vscale, lane);
+  finish<D, G>(st, a, s, g, nsplit == 1, int64_t(sg) * a.max_splits + split, qk_scale, vscale, lane);
 }
 
 // ---- auto: contiguous equal shares of the flattened block space ------------------------
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_W
     run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, b0, b1,
                              t_end, L, a.cache.log2_page, Hkv * tile_b, g * tile_b, lane);
     const bool complete = b0 == 0 && b1 == nb;
-    finish<D, G>(st, a, s, g, complete, int64_t(w) * 2 + (first ? 0 : 1), vscale, lane);
+    finish<D, G>(st, a, s, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
     first = false;
     f = gs + b1;
     if (g + 1 == Hkv) {

@@ -247,9 +247,14 @@ __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__
   }
 }
 
-// Online-softmax state of one wave: running max m (log2 units, per head lane), the
-// lane's share of the running sum, and the output accumulator O [16 heads x D]
-// (lane (n, c) holds heads 4c..4c+3 of dim 16*dt + n in O[dt]).
+// Online-softmax state of one wave: running max m of the raw scores q.k (per row
+// lane), the lane's share of the running sum of exp2((z - m) * scale) and the output
+// accumulator O [16 rows x D] (lane (n, c) holds rows 4c..4c+3 of dim 16*dt + n in
+// O[dt]).  m starts at a large finite negative value rather than -inf: a row whose
+// scores so far are all masked (-inf) then gets weight exp2(-inf) = 0 with no special
+// case, and keeps l = 0.
+constexpr float kMInit = -1e30f;
+
 template <int D>
 struct State {
   float m, l;
@@ -258,10 +263,20 @@ struct State {
 
 template <int D>
 __device__ __forceinline__ void state_init(State<D>& st) {
-  st.m = -INFINITY;
+  st.m = kMInit;
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// 2^x on the hardware exponential unit (results below the normal range flush to 0,
+// which for softmax weights below 2^-126 of the row maximum is what the sum keeps).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Natural-log log-sum-exp of a row from its state: m * scale (log2 units) + log2 l;
+// -inf when the row saw no key.
+__device__ __forceinline__ float row_lse(float m, float l, float scale) {
+  return l > 0.f ? (m * scale + __log2f(l)) * kLn2 : -INFINITY;
 }
 
 // Q^T operand of query row `row`, kv head g: lane (n, c) holds dims 32j + 8c .. +7 of
@@ -384,11 +399,10 @@ __device__ __forceinline__ void scales(const AttnArgs& a, int g, float& qk_scale
   }
 }
 
-// Scores^T of one block for one tile of 16 query rows, scaled to log2 units: lane
-// (n, c) gets row n's scores of block tokens tok_of(c, e), e = 0..7.
+// Raw scores^T q.k of one block for one tile of 16 query rows: lane (n, c) gets row
+// n's scores of block tokens tok_of(c, e), e = 0..7.
 template <int D>
-__device__ __forceinline__ void block_scores(const Block<D>& b, const bf16x8 (&qf)[D / 32],
-                                             float qk_scale, float (&sc)[8]) {
+__device__ __forceinline__ void block_scores(const Block<D>& b, const bf16x8 (&qf)[D / 32], float (&sc)[8]) {
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
@@ -397,8 +411,8 @@ __device__ __forceinline__ void block_scores(const Block<D>& b, const bf16x8 (&q
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sc[i] = sa[i] * qk_scale;
-    sc[4 + i] = sb[i] * qk_scale;
+    sc[i] = sa[i];
+    sc[4 + i] = sb[i];
   }
 }
 
@@ -421,11 +435,13 @@ __device__ __forceinline__ void mask_v_tail(Block<D>& b, int nvalid, int lane) {
   }
 }
 
-// Online-softmax update with this block's (masked) scores, then O += P . V.  A row
-// whose every score so far is masked keeps m = -inf, l = 0 and O = 0.
+// Online-softmax update with this block's raw (masked: -inf) scores, then O += P . V.
+// `scale` turns raw scores into log2 units (softmax scale x log2 e, x the K dequant
+// scale for FP8 caches); it is positive, so maxima of raw scores are maxima of the
+// scaled ones and the scaling folds into one FMA per score.
 template <int D>
 __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, const float (&sc)[8],
-                                           int lane) {
+                                           float scale, int lane) {
   const int c = lane >> 4;
   float bm = sc[0];
 #pragma unroll
@@ -433,12 +449,12 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
   const float mn = fmaxf(st.m, bm);
-  const bool none = mn == -INFINITY;
-  const float alpha = none ? 1.f : exp2f(st.m - mn);  // 0 on a row's first live block
+  const float alpha = fast_exp2((st.m - mn) * scale);  // 0 on a row's first live block
+  const float off = -mn * scale;
   float p[8], ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = none ? 0.f : exp2f(sc[e] - mn);
+    p[e] = fast_exp2(__builtin_fmaf(sc[e], scale, off));
     ps += p[e];
   }
   st.l = st.l * alpha + ps;

@@ -38,7 +38,8 @@ struct PfGeom {
 // log-sum-exp; several: partial record (row, kv head, split) for the merge kernel.
 template <int D, int G, int NT>
 __device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D> (&st)[NT], int q0, int C,
-                                               int cq0, int g, int split, float vscale, int lane) {
+                                               int cq0, int g, int split, float qk_scale, float vscale,
+                                               int lane) {
   constexpr int QPT = PfGeom<G>::QPT;
   const int n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
@@ -47,7 +48,7 @@ __device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D>
     float l = st[r].l;
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const float lse = l > 0.f ? (st[r].m + __log2f(l)) * kLn2 : -INFINITY;  // row n
+    const float lse = row_lse(st[r].m, l, qk_scale);  // row n
     float inv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -142,18 +143,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
           for (int r = 0; r < NT; ++r) {
             float sc[8];
-            block_scores<D>(blk, qf[r], qk_scale, sc);
+            block_scores<D>(blk, qf[r], sc);
             if (t + BT > lim_min) {  // wave-uniform: the block reaches some row's position
 #pragma unroll
               for (int e = 0; e < 8; ++e)
                 if (t + tok_of(c, e) >= lim[r]) sc[e] = -INFINITY;
             }
-            softmax_pv<D>(st[r], blk, sc, lane);
+            softmax_pv<D>(st[r], blk, sc, qk_scale, lane);
           }
         });
   }
 
-  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, vscale, lane);
+  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane);
 }
 
 // ---- LDS-shared variant (pages of >= 32 tokens) -----------------------------------------
@@ -290,17 +291,24 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
       r[k] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
+  // bf16 stages are swizzled against LDS bank conflicts: in every 64-byte row (32
+  // tokens of a K chunk or of a V dim), 16-byte segment c of row r is stored at
+  // segment c ^ ((r >> 2) & 3), so the 16 rows one operand load touches spread over
+  // all banks.  The copy writes and the operand reads apply the same map.
+  const uint32_t wofs = esz == 2 ? uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 4) & 3)))
+                                 : uint32_t(lane * 16);
   auto stash = [&](const uint4 (&r)[SL::PER_WAVE], int stage) {
     char* dst = smem + stage * SL::BYTES;
 #pragma unroll
     for (int k = 0; k < SL::PER_WAVE; ++k) {
       if (!SL::EVEN && w + k * kPfWaves >= SL::PIECES) break;
-      *reinterpret_cast<uint4*>(dst + (w + k * kPfWaves) * 1024 + lane * 16) = r[k];
+      *reinterpret_cast<uint4*>(dst + (w + k * kPfWaves) * 1024 + wofs) = r[k];
     }
   };
 
   const int nblk = b1 - b0;
-  const uint32_t lk = uint32_t((n * 32 + 8 * c) * esz);  // lane offset in a K chunk / V tile
+  // lane offset of the operand load in a K chunk / V tile (row n, segment c)
+  const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 2) & 3))) : uint32_t(n * 32 + 8 * c);
   // Fold block b0+i from stage i%2 (the wave's rows only need blocks below kend_w).
   auto compute = [&](int i) {
     const int t = (b0 + i) << LOG2_BT;
@@ -318,13 +326,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
       float sc[8];
-      block_scores<D>(b, qf[r], qk_scale, sc);
+      block_scores<D>(b, qf[r], sc);
       if (t + BT > lim_min) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (t + tok_of(c, e) >= lim[r]) sc[e] = -INFINITY;
       }
-      softmax_pv<D>(st[r], b, sc, lane);
+      softmax_pv<D>(st[r], b, sc, qk_scale, lane);
     }
   };
   // Register slots hold the next blocks: ra the even-numbered, rb the odd-numbered
@@ -355,7 +363,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   }
   if (i < nblk) compute(i);
   if (!live) return;
-  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, vscale, lane);
+  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane);
 }
 
 // Merge of the key splits of one (query row, kv head).
