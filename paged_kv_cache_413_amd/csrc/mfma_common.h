@@ -438,7 +438,13 @@ __device__ __forceinline__ void mask_v_tail(Block<D>& b, int nvalid, int lane) {
 // Online-softmax update with this block's raw (masked: -inf) scores, then O += P . V.
 // `scale` turns raw scores into log2 units (softmax scale x log2 e, x the K dequant
 // scale for FP8 caches); it is positive, so maxima of raw scores are maxima of the
-// scaled ones and the scaling folds into one FMA per score.
+// scaled ones and the scaling folds into one FMA per score.  A row keeps its
+// reference maximum m until a block's maximum exceeds it by more than
+// kRescaleLog2 (log2 units): weights up to 2^kRescaleLog2 are exact enough in fp32
+// and bf16 alike, l and O always share the reference, and O is rescaled only on the
+// rare blocks that move some row's reference.
+constexpr float kRescaleLog2 = 8.f;
+
 template <int D>
 __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, const float (&sc)[8],
                                            float scale, int lane) {
@@ -448,17 +454,18 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
   for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
   bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
   bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-  const float mn = fmaxf(st.m, bm);
-  const float alpha = fast_exp2((st.m - mn) * scale);  // 0 on a row's first live block
-  const float off = -mn * scale;
+  const bool grow = (bm - st.m) * scale > kRescaleLog2;  // same in the 4 lanes of a row
+  const float mref = grow ? bm : st.m;
+  const float off = -mref * scale;
   float p[8], ps = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     p[e] = fast_exp2(__builtin_fmaf(sc[e], scale, off));
     ps += p[e];
   }
-  st.l = st.l * alpha + ps;
-  if (__ballot(mn != st.m)) {  // some row's max moved: rescale O by that row's alpha
+  if (__ballot(grow)) {  // some row moved its reference: rescale its l and O
+    const float alpha = fast_exp2((st.m - mref) * scale);  // 1 for rows that did not move
+    st.l *= alpha;
     float al[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * c + i, 64);
@@ -466,8 +473,9 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
     for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.o[dt][i] *= al[i];
+    st.m = mref;
   }
-  st.m = mn;
+  st.l += ps;
   Frag8 pa;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
