@@ -484,6 +484,64 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = mma(pa.v, b.v[dt], st.o[dt]);
 }
 
+// The same update for NT tiles of 16 rows that share one block: all scores first,
+// then all exponentials, one vote for the rare rescale, then all P.V products, so
+// that one tile's MFMAs and another's vector work can overlap.  sc[r] holds tile r's
+// raw (masked) scores.
+template <int D, int NT>
+__device__ __forceinline__ void softmax_pv_tiles(State<D> (&st)[NT], const Block<D>& b,
+                                                 const float (&sc)[NT][8], float scale, int lane) {
+  const int c = lane >> 4;
+  bool grow[NT];
+  float mref[NT];
+  Frag8 pa[NT];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    float bm = sc[r][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[r][e]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
+    mref[r] = grow[r] ? bm : st[r].m;
+    any |= grow[r];
+    const float off = -mref[r] * scale;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(__builtin_fmaf(sc[r][e], scale, off));
+      ps += p[e];
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      pa[r].w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));
+    // rescale of l by a moved reference happens below; add this block's sum after it
+    if (!grow[r]) st[r].l += ps;
+    else {
+      st[r].l = st[r].l * fast_exp2((st[r].m - mref[r]) * scale) + ps;
+    }
+  }
+  if (__ballot(any)) {
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      const float alpha = fast_exp2((st[r].m - mref[r]) * scale);  // 1 for rows that did not move
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * c + i, 64);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[r].o[dt][i] *= al[i];
+      st[r].m = mref[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st[r].o[dt] = mma(pa[r].v, b.v[dt], st[r].o[dt]);
+}
+
 // Blocks [b0, b1) of one (sequence, kv head), folded in order by fold(block, t0).
 // PKV_DECODE_DEPTH register buffers rotate: while block i is folded the loads of the
 // next DEPTH-1 blocks are in flight.  Inside the loop every prefetch is

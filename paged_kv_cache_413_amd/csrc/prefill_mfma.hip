@@ -323,17 +323,17 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) b.v[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
     if (t + BT > L) mask_v_tail<D>(b, L - t, lane);
+    float sc[NT][8];
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
-      float sc[8];
-      block_scores<D>(b, qf[r], sc);
-      if (t + BT > lim_min) {
+    for (int r = 0; r < NT; ++r) block_scores<D>(b, qf[r], sc[r]);
+    if (t + BT > lim_min) {  // wave-uniform: the block reaches some row's position
+#pragma unroll
+      for (int r = 0; r < NT; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (t + tok_of(c, e) >= lim[r]) sc[e] = -INFINITY;
-      }
-      softmax_pv<D>(st[r], b, sc, qk_scale, lane);
+          if (t + tok_of(c, e) >= lim[r]) sc[r][e] = -INFINITY;
     }
+    softmax_pv_tiles<D, NT>(st, b, sc, qk_scale, lane);
   };
   // Register slots hold the next blocks: ra the even-numbered, rb the odd-numbered
   // ones.  At step i, block i+1 goes from its slot into stage (i+1)%2 -- last read
