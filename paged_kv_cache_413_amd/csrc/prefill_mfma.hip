@@ -293,9 +293,12 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   };
   // bf16 stages are swizzled against LDS bank conflicts: in every 64-byte row (32
   // tokens of a K chunk or of a V dim), 16-byte segment c of row r is stored at
-  // segment c ^ ((r >> 2) & 3), so the 16 rows one operand load touches spread over
-  // all banks.  The copy writes and the operand reads apply the same map.
-  const uint32_t wofs = esz == 2 ? uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 4) & 3)))
+  // segment c ^ ((r >> 1) & 3).  A 16-byte-per-lane read is served 8 lanes at a time
+  // from a 128-byte bank window; the operand load's 8 lanes read 8 consecutive rows
+  // (two per window position), and the map spreads them over all of it (measured
+  // conflict-free; the plain layout costs 4 extra cycles per read).  The copy writes
+  // and the operand reads apply the same map.
+  const uint32_t wofs = esz == 2 ? uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 3) & 3)))
                                  : uint32_t(lane * 16);
   auto stash = [&](const uint4 (&r)[SL::PER_WAVE], int stage) {
     char* dst = smem + stage * SL::BYTES;
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
 
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
-  const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 2) & 3))) : uint32_t(n * 32 + 8 * c);
+  const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3))) : uint32_t(n * 32 + 8 * c);
   // Fold block b0+i from stage i%2 (the wave's rows only need blocks below kend_w).
   auto compute = [&](int i) {
     const int t = (b0 + i) << LOG2_BT;
