@@ -369,13 +369,45 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane);
 }
 
-// Merge of the key splits of one (query row, kv head).
+// Merge of the key splits: one thread per float4 of the output (query row, kv head g,
+// head h, 4 dims), combining the nsplit records with log-sum-exp weights; the thread
+// at dim 0 writes the row's log-sum-exp.  Records of a split that saw no key of the
+// row (lse = -inf) weigh nothing.
+constexpr int kPfMergeThreads = 256;
+
 template <int D, int G>
-__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kPfMergeThreads) void prefill_merge_kernel(AttnArgs a) {
+  constexpr int CH = G * D / 4;  // float4 chunks per (row, kv head)
   const int Hkv = a.cache.num_kv_heads, nsplit = a.max_splits;
-  const int row = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
-  const int64_t r0 = (int64_t(row) * Hkv + g) * nsplit;
-  merge_partials<D, G>(a, row, g, nsplit, [r0](int i) { return r0 + i; });
+  const int64_t idx = int64_t(blockIdx.x) * kPfMergeThreads + threadIdx.x;
+  if (idx >= int64_t(a.total_q) * Hkv * CH) return;
+  const int ch = int(idx % CH);
+  const int64_t rg = idx / CH;  // row * Hkv + g
+  const int g = int(rg % Hkv);
+  const int64_t row = rg / Hkv;
+  const int e = ch * 4, h = e / D, d = e % D;
+  float m = -INFINITY, w = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < nsplit; ++i) {
+    const int64_t rec = rg * nsplit + i;
+    const float x = a.ws_lse[rec * G + h];
+    const float4 o = *reinterpret_cast<const float4*>(a.ws_o + rec * (G * D) + e);
+    if (x == -INFINITY) continue;
+    const float mn = fmaxf(m, x);
+    const float sa = __expf(m - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
+    acc.x = acc.x * sa + o.x * sb;
+    acc.y = acc.y * sa + o.y * sb;
+    acc.z = acc.z * sa + o.z * sb;
+    acc.w = acc.w * sa + o.w * sb;
+    w = w * sa + sb;
+    m = mn;
+  }
+  const float inv = 1.f / w;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + (row * a.num_q_heads + g * G + h) * D + d;
+  const uint32_t lo = f32_to_bf16(acc.x * inv) | (f32_to_bf16(acc.y * inv) << 16);
+  const uint32_t hi = f32_to_bf16(acc.z * inv) | (f32_to_bf16(acc.w * inv) << 16);
+  *reinterpret_cast<uint2*>(out) = make_uint2(lo, hi);
+  if (a.lse_out && d == 0) a.lse_out[row * a.num_q_heads + g * G + h] = m + __logf(w);
 }
 
 template <int KV, int D, int G, bool SMALLP>
@@ -389,8 +421,9 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
-  hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(unsigned(int64_t(a.total_q) * a.cache.num_kv_heads)),
-                     dim3(kMergeThreads), 0, st, a);
+  const int64_t threads = int64_t(a.total_q) * a.cache.num_kv_heads * (G * D / 4);
+  hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(unsigned((threads + kPfMergeThreads - 1) / kPfMergeThreads)),
+                     dim3(kPfMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 
