@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <algorithm>
+#include <cstdlib>
 #include <map>
 #include <mutex>
 #include <string>
@@ -156,6 +157,18 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 constexpr int kMinShareBlocks = 4;  // auto schedule: at least 4 x 32 tokens per wave
 
+// Waves of the balanced schedule: the device's resident count, or PKV_AUTO_WAVES=N
+// (1 <= N <= 65536; for tests and tuning: few waves give long shares and many cut
+// segments on small batches).  Read on every plan, so the size query and the call must
+// see the same value.
+int auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
+  if (const char* e = std::getenv("PKV_AUTO_WAVES")) {
+    const long n = std::strtol(e, nullptr, 10);
+    if (n >= 1 && n <= (1L << 16)) return int(n);
+  }
+  return std::max(1, pkv::mfma_auto_waves(kv_dtype, head_dim, group, page_size));
+}
+
 // Partition plan of one decode call.
 //  * Matrix-core path (bf16 / FP8 caches, bf16 queries, pages >= 8 tokens):
 //    num_splits == 0 spreads all (sequence, kv head, 32-token block) work evenly over
@@ -175,7 +188,7 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
   p.mfma = pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, P);
   if (p.mfma && num_splits == 0) {
     p.auto_mode = true;
-    p.waves = std::max(1, pkv::mfma_auto_waves(c.dtype, c.head_dim, G, P));
+    p.waves = auto_waves(c.dtype, c.head_dim, G, P);
     p.chunk = 0;
     p.max_splits = 0;
     const size_t recs = size_t(2) * p.waves;  // up to two cut segments per wave

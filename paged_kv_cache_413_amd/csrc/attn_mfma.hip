@@ -33,6 +33,8 @@
 // to finish a piece, needs agent-scope release/acquire fences; on this chip those
 // write back and invalidate a whole L2 per piece, which costs far more than the
 // second launch.)
+#include <algorithm>
+
 #include "mfma_common.h"
 
 namespace pkv {
@@ -244,18 +246,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_W
 }
 
 // Merge of one cut (sequence, kv head) segment of the balanced schedule, by the
-// workgroup of the wave that holds its last piece (a wave is the last one of at
+// workgroup that takes the wave holding its last piece (a wave is the last one of at
 // most one cut segment: its first).  The pieces are in waves w0 .. w; the record of
-// wave v is slot 0, except slot 1 for w0 when the segment is not w0's first.
+// wave v is slot 0, except slot 1 for w0 when the segment is not w0's first.  A fixed
+// grid of one-wave workgroups walks the waves' descriptors (most name no merge).
+constexpr int kAutoMergeThreads = 64;
+constexpr int kAutoMergeGrid = 512;
+
 template <int D, int G>
-__global__ __launch_bounds__(kMergeThreads) void merge_auto_kernel(AttnArgs a) {
-  const int w = blockIdx.x;
-  const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
-  if (d.x < 0 || !(d.w & 1)) return;
-  const int64_t w0 = d.z;
-  const bool slot1 = d.w & 2;
-  merge_partials<D, G>(a, d.x, d.y, int(w - w0 + 1),
-                       [w0, slot1](int i) { return (w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0); });
+__global__ __launch_bounds__(kAutoMergeThreads) void merge_auto_kernel(AttnArgs a) {
+  for (int w = blockIdx.x; w < a.num_waves; w += gridDim.x) {
+    const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
+    if (d.x < 0 || !(d.w & 1)) continue;
+    const int w0 = d.z;
+    const bool slot1 = d.w & 2;
+    merge_partials<D, G, kAutoMergeThreads>(a, d.x, d.y, w - w0 + 1, [w0, slot1](int i) {
+      return int64_t(w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0);
+    });
+  }
 }
 
 // Merge of the fixed partitions of one (sequence, kv head).
@@ -267,7 +275,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) 
   const int n = (a.seqs.context_lens[s] + a.chunk - 1) / a.chunk;
   if (n <= 1) return;  // written directly
   const int64_t r0 = int64_t(sg) * a.max_splits;
-  merge_partials<D, G>(a, s, g, n, [r0](int i) { return r0 + i; });
+  merge_partials<D, G, kMergeThreads>(a, s, g, n, [r0](int i) { return r0 + i; });
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -278,7 +286,8 @@ hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
     hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP>), dim3(p.waves), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(p.waves), dim3(kMergeThreads), 0, st, a);
+    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(unsigned(std::min(p.waves, kAutoMergeGrid))),
+                       dim3(kAutoMergeThreads), 0, st, a);
     return hipGetLastError();
   }
   const int64_t nblk = int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads * a.max_splits;

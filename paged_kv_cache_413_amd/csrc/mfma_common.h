@@ -33,8 +33,11 @@ constexpr int LOG2_BT = 5;
 #define PKV_KV_LOAD_AUX 0
 #endif
 // Waves per SIMD the decode kernels are compiled for (register budget 512 / this).
+// One: two waves on a SIMD split its share of the bandwidth unevenly (the older one
+// issues first and runs about twice as fast while both are active), and with 1024
+// single waves the two HBM-bound loads measure 5 % faster than with 2048.
 #ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 2
+#define PKV_DECODE_WAVES_PER_EU 1
 #endif
 // Blocks whose loads are in flight while one is folded, plus one (2 or 3 buffers).
 #ifndef PKV_DECODE_DEPTH
@@ -301,22 +304,20 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restr
 
 // Merge the n partial records of one (query row, kv head) -- record i is rec(i) --
 // into the final output and log-sum-exp: LSE_h = log sum_i exp(lse_ih),
-// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  One 256-thread workgroup: every thread
+// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  One workgroup of NT threads: every thread
 // owns float4 chunks of the G x D record (one head each) and a stride of records,
 // and keeps a running (max, sum of weights, weighted sum) over them, so the loads
 // of different records are independent and in flight together; the record-parallel
-// states are then combined in LDS.
+// states are then combined in LDS.  Every thread of the workgroup must call it (it
+// may hold barriers); it may be called repeatedly.
 constexpr int kMergeThreads = 256;
 
-template <int D, int G, typename RecFn>
+template <int D, int G, int NT, typename RecFn>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g, int n, RecFn rec) {
-  constexpr int NT = kMergeThreads;
   constexpr int C = G * D / 4;                  // float4 chunks per record
   constexpr int CC = C < NT ? C : NT;           // chunk lanes
   constexpr int RP = NT / CC;                   // record-parallel factor
   constexpr int CPT = (C + NT - 1) / NT;        // chunks per thread
-  __shared__ float4 s_acc[RP][CC * CPT];
-  __shared__ float s_m[RP][CC * CPT], s_w[RP][CC * CPT];
   const int t = threadIdx.x;
   const int cl = t % CC, rp = t / CC;
   float4 acc[CPT];
@@ -349,6 +350,8 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g
     }
   }
   if constexpr (RP > 1) {
+    __shared__ float4 s_acc[RP][CC * CPT];
+    __shared__ float s_m[RP][CC * CPT], s_w[RP][CC * CPT];
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       s_acc[rp][cl + k * CC] = acc[k];
@@ -356,35 +359,39 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g
       s_w[rp][cl + k * CC] = w[k];
     }
     __syncthreads();
-    if (rp != 0) return;
+    if (rp == 0) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      for (int q = 1; q < RP; ++q) {
-        const float mo = s_m[q][cl + k * CC];
-        if (mo == -INFINITY) continue;  // that lane had no records
-        const float4 o = s_acc[q][cl + k * CC];
-        const float mn = fmaxf(m[k], mo);
-        const float sa = __expf(m[k] - mn), sb = __expf(mo - mn);
-        acc[k].x = acc[k].x * sa + o.x * sb;
-        acc[k].y = acc[k].y * sa + o.y * sb;
-        acc[k].z = acc[k].z * sa + o.z * sb;
-        acc[k].w = acc[k].w * sa + o.w * sb;
-        w[k] = w[k] * sa + s_w[q][cl + k * CC] * sb;
-        m[k] = mn;
+      for (int k = 0; k < CPT; ++k) {
+        for (int q = 1; q < RP; ++q) {
+          const float mo = s_m[q][cl + k * CC];
+          if (mo == -INFINITY) continue;  // that lane had no records
+          const float4 o = s_acc[q][cl + k * CC];
+          const float mn = fmaxf(m[k], mo);
+          const float sa = __expf(m[k] - mn), sb = __expf(mo - mn);
+          acc[k].x = acc[k].x * sa + o.x * sb;
+          acc[k].y = acc[k].y * sa + o.y * sb;
+          acc[k].z = acc[k].z * sa + o.z * sb;
+          acc[k].w = acc[k].w * sa + o.w * sb;
+          w[k] = w[k] * sa + s_w[q][cl + k * CC] * sb;
+          m[k] = mn;
+        }
       }
     }
+    __syncthreads();  // the LDS states may be rewritten by the next call
   }
+  if (rp == 0) {
 #pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int e = (cl + k * CC) * 4;
-    if (e < G * D) {
-      const int h = e / D, d = e % D;
-      const float inv = 1.f / w[k];
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G + h) * D + d;
-      const uint32_t lo = f32_to_bf16(acc[k].x * inv) | (f32_to_bf16(acc[k].y * inv) << 16);
-      const uint32_t hi = f32_to_bf16(acc[k].z * inv) | (f32_to_bf16(acc[k].w * inv) << 16);
-      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-      if (a.lse_out && d == 0) a.lse_out[int64_t(row) * a.num_q_heads + g * G + h] = m[k] + __logf(w[k]);
+    for (int k = 0; k < CPT; ++k) {
+      const int e = (cl + k * CC) * 4;
+      if (e < G * D) {
+        const int h = e / D, d = e % D;
+        const float inv = 1.f / w[k];
+        uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G + h) * D + d;
+        const uint32_t lo = f32_to_bf16(acc[k].x * inv) | (f32_to_bf16(acc[k].y * inv) << 16);
+        const uint32_t hi = f32_to_bf16(acc[k].z * inv) | (f32_to_bf16(acc[k].w * inv) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+        if (a.lse_out && d == 0) a.lse_out[int64_t(row) * a.num_q_heads + g * G + h] = m[k] + __logf(w[k]);
+      }
     }
   }
 }

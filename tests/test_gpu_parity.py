@@ -207,6 +207,47 @@ def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
     assert_lse_close(lse, ref[1], "bf16", f"P={P}")
 
 
+AUTO_WAVES = [
+    # (waves, workload, overrides): few waves, so shares are long and spread over
+    # several (sequence, kv head) segments, and segments over several waves
+    (3, 2, dict(lens=[1, 63, 700, 2100, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
+                head_dim=128)),
+    (16, 2, dict(lens=[1, 63, 700, 2100, 33], page_size=32, num_q_heads=8, num_kv_heads=8,
+                 head_dim=64)),                                    # G = 1
+    (12, 2, dict(lens=[5, 40, 333, 1000, 17, 64], page_size=16, num_q_heads=16, num_kv_heads=2,
+                 head_dim=64)),                                    # G = 8, pages of 16
+    (40, 2, dict(lens=[1, 31, 32, 33, 95, 300, 4000], page_size=8, num_q_heads=128,
+                 num_kv_heads=8, head_dim=128)),                   # G = 16, pages of 8
+    (20, 5, dict(num_seqs=6, group_size=3, prefix_len=128, len_range=(129, 600))),  # fp8 KV
+    (1, 2, dict(lens=[1, 700, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
+                head_dim=128)),                                    # one wave does it all
+]
+
+
+@pytest.mark.parametrize("waves,cfg,over", AUTO_WAVES)
+def test_auto_decode_few_waves(gpu_lib, monkeypatch, waves, cfg, over):
+    """The balanced decode schedule with few waves (PKV_AUTO_WAVES): long shares that
+    cross many segment boundaries and segments cut over several waves match the
+    oracle, and a second call gives the same bits."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    monkeypatch.setenv("PKV_AUTO_WAVES", str(waves))
+    wl = workloads.make(cfg, num_splits=0, **over)
+    print(f"[case] auto waves={waves} cfg={cfg} {over}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, lse, _, _ = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(dec, ref[0], wl.kv_dtype, f"waves={waves}")
+    assert_lse_close(lse, ref[1], wl.kv_dtype, f"waves={waves}")
+    first = [db.out_dec.clone(), db.lse_dec.clone()]
+    db.decode_step()
+    torch.cuda.synchronize()
+    assert torch.equal(first[0].view(torch.int16), db.out_dec.view(torch.int16))
+    assert torch.equal(first[1].view(torch.int32), db.lse_dec.view(torch.int32))
+
+
 PREFILL_EDGES = [
     # (page_size, chunks, cached, num_q_heads, num_kv_heads, head_dim)
     (64, [1, 15, 16, 17], [0, 0, 5, 100], 32, 8, 128),       # first chunks: triangular
