@@ -39,7 +39,8 @@ WORKLOADS = {
     "long_context_splitkv_bf16": 4,
     "fp8_shared_prefix_decode": 5,
 }
-KERNEL_SOURCES = ("attn_valu.hip", "attn_mfma.hip", "append.hip", "device_common.h", "api.cpp")
+# sources of the decode call on the matrix-core path (the traffic record is void once any changes)
+KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp")
 
 
 def kernel_source_hash() -> str:

@@ -33,8 +33,6 @@
 // to finish a piece, needs agent-scope release/acquire fences; on this chip those
 // write back and invalidate a whole L2 per piece, which costs far more than the
 // second launch.)
-#include <algorithm>
-
 #include "mfma_common.h"
 
 namespace pkv {
@@ -114,13 +112,24 @@ __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, in
   if (c == 0 && nn < G) a.ws_lse[rec * G + nn] = lse;
 }
 
+// Independent waves per workgroup of the decode kernels (no LDS, no barriers: a larger
+// workgroup only packs them onto one CU, one per SIMD).  Placing 1024 one-wave
+// workgroups takes the dispatcher about 4 us, but packing 2 or 4 measured no faster:
+// the waves placed first already keep HBM busy.
+#ifndef PKV_DECODE_WG_WAVES
+#define PKV_DECODE_WG_WAVES 1
+#endif
+constexpr int kWgWaves = PKV_DECODE_WG_WAVES;
+
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
-  const int lane = threadIdx.x;
-  const int split = blockIdx.x % a.max_splits;
-  const int sg = blockIdx.x / a.max_splits;
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = int64_t(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
   const int Hkv = a.cache.num_kv_heads;
+  if (wid >= int64_t(a.seqs.num_seqs) * Hkv * a.max_splits) return;
+  const int split = int(wid % a.max_splits);
+  const int sg = int(wid / a.max_splits);
   const int g = sg % Hkv, s = sg / Hkv;
   const int L = a.seqs.context_lens[s];
   const int t0 = split * a.chunk;
@@ -187,9 +196,10 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, int S, 
 }
 
 template <int KV, int D, int G, bool SMALLP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
-  const int lane = threadIdx.x;
-  const int w = blockIdx.x;
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * kWgWaves + (threadIdx.x >> 6);
+  if (w >= a.num_waves) return;
   const int S = a.seqs.num_seqs, Hkv = a.cache.num_kv_heads;
   const int32_t* lens = a.seqs.context_lens;
   const int64_t T = total_blocks(lens, S, Hkv, lane);
@@ -246,24 +256,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_W
 }
 
 // Merge of one cut (sequence, kv head) segment of the balanced schedule, by the
-// workgroup that takes the wave holding its last piece (a wave is the last one of at
-// most one cut segment: its first).  The pieces are in waves w0 .. w; the record of
-// wave v is slot 0, except slot 1 for w0 when the segment is not w0's first.  A fixed
-// grid of one-wave workgroups walks the waves' descriptors (most name no merge).
-constexpr int kAutoMergeThreads = 64;
-constexpr int kAutoMergeGrid = 512;
+// workgroup of the wave that holds its last piece (a wave is the last one of at most
+// one cut segment: its first).  The pieces are in waves w0 .. w; the record of wave v
+// is slot 0, except slot 1 for w0 when the segment is not w0's first.  One workgroup
+// per wave (most find nothing to do and exit at once): a loop over several
+// descriptors per workgroup would chain their dependent loads.
+#ifndef PKV_AUTO_MERGE_THREADS
+#define PKV_AUTO_MERGE_THREADS 256
+#endif
+constexpr int kAutoMergeThreads = PKV_AUTO_MERGE_THREADS;
 
 template <int D, int G>
 __global__ __launch_bounds__(kAutoMergeThreads) void merge_auto_kernel(AttnArgs a) {
-  for (int w = blockIdx.x; w < a.num_waves; w += gridDim.x) {
-    const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
-    if (d.x < 0 || !(d.w & 1)) continue;
-    const int w0 = d.z;
-    const bool slot1 = d.w & 2;
-    merge_partials<D, G, kAutoMergeThreads>(a, d.x, d.y, w - w0 + 1, [w0, slot1](int i) {
-      return int64_t(w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0);
-    });
-  }
+  const int w = blockIdx.x;
+  const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
+  if (d.x < 0 || !(d.w & 1)) return;
+  const int w0 = d.z;
+  const bool slot1 = d.w & 2;
+  merge_partials<D, G, kAutoMergeThreads>(a, d.x, d.y, w - w0 + 1, [w0, slot1](int i) {
+    return int64_t(w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0);
+  });
 }
 
 // Merge of the fixed partitions of one (sequence, kv head).
@@ -283,15 +295,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) 
 template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
   if (p.auto_mode) {
-    hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP>), dim3(p.waves), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP>), dim3(unsigned((p.waves + kWgWaves - 1) / kWgWaves)),
+                       dim3(64 * kWgWaves), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(unsigned(std::min(p.waves, kAutoMergeGrid))),
-                       dim3(kAutoMergeThreads), 0, st, a);
+    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(p.waves), dim3(kAutoMergeThreads), 0, st, a);
     return hipGetLastError();
   }
   const int64_t nblk = int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads * a.max_splits;
-  hipLaunchKernelGGL((decode_fixed_kernel<KV, D, G, SMALLP>), dim3(unsigned(nblk)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_fixed_kernel<KV, D, G, SMALLP>), dim3(unsigned((nblk + kWgWaves - 1) / kWgWaves)),
+                     dim3(64 * kWgWaves), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL((merge_fixed_kernel<D, G>), dim3(unsigned(int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads)),
@@ -352,7 +365,7 @@ int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
                                         : auto_kernel_for<DT_BF16, 128>(group, smallp))
                       : (head_dim == 64 ? auto_kernel_for<DT_FP8, 64>(group, smallp)
                                         : auto_kernel_for<DT_FP8, 128>(group, smallp));
-  return resident_blocks(k, 64);
+  return resident_blocks(k, 64 * kWgWaves) * kWgWaves;
 }
 
 hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
