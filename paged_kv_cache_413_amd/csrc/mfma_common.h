@@ -442,6 +442,21 @@ __device__ __forceinline__ void mask_v_tail(Block<D>& b, int nvalid, int lane) {
   }
 }
 
+// Maximum of x over the four lanes of a score row (lanes n, n+16, n+32, n+48), in all
+// four: two lane swaps across 32 and 16 lanes (no LDS permute, no lane arithmetic).
+// The swaps' results are copied out of their vector before the bit casts: a bit cast
+// applied to an element of that vector type reads element 0 whatever the index.
+__device__ __forceinline__ float row_max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // x[l mod 32] | x[32 + l mod 32]
+  const uint32_t a0 = a[0], a1 = a[1];
+  const float y = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 2k | 2k+1
+  const uint32_t b0 = b[0], b1 = b[1];
+  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+}
+
 // Online-softmax update with this block's raw (masked: -inf) scores, then O += P . V.
 // `scale` turns raw scores into log2 units (softmax scale x log2 e, x the K dequant
 // scale for FP8 caches); it is positive, so maxima of raw scores are maxima of the
@@ -459,8 +474,7 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
   float bm = sc[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-  bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+  bm = row_max4(bm);
   const bool grow = (bm - st.m) * scale > kRescaleLog2;  // same in the 4 lanes of a row
   const float mref = grow ? bm : st.m;
   const float off = -mref * scale;
@@ -491,25 +505,81 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
   for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = mma(pa.v, b.v[dt], st.o[dt]);
 }
 
-// The same update for NT tiles of 16 rows that share one block: all scores first,
-// then all exponentials, one vote for the rare rescale, then all P.V products, so
-// that one tile's MFMAs and another's vector work can overlap.  sc[r] holds tile r's
-// raw (masked) scores.
+// The same update split in two for NT tiles of 16 rows that share one block, so that
+// the caller can put other work (the next block's scores) between and around them.
+// softmax_head: the maxima, the vote and the rare rescale of l and O (a branch);
+// off[r] = -m * scale of each row's reference.  softmax_tail: the weights of the
+// block (straight-line vector code), their sum into l, and the P operands pa.
 template <int D, int NT>
-__device__ __forceinline__ void softmax_pv_tiles(State<D> (&st)[NT], const Block<D>& b,
-                                                 const float (&sc)[NT][8], float scale, int lane) {
+__device__ __forceinline__ void softmax_head(State<D> (&st)[NT], const float (&sc)[NT][8], float scale,
+                                             float (&off)[NT], int lane) {
   const int c = lane >> 4;
   bool grow[NT];
   float mref[NT];
-  Frag8 pa[NT];
   bool any = false;
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
     float bm = sc[r][0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[r][e]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    bm = row_max4(bm);
+    grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
+    mref[r] = grow[r] ? bm : st[r].m;
+    any |= grow[r];
+    off[r] = -mref[r] * scale;
+  }
+  if (__ballot(any)) {
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+      const float alpha = fast_exp2((st[r].m - mref[r]) * scale);  // 1 for rows that did not move
+      st[r].l *= alpha;
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * c + i, 64);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[r].o[dt][i] *= al[i];
+      st[r].m = mref[r];
+    }
+  }
+}
+
+template <int NT, typename StateT>
+__device__ __forceinline__ void softmax_tail(StateT (&st)[NT], const float (&sc)[NT][8], float scale,
+                                             const float (&off)[NT], Frag8 (&pa)[NT]) {
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(__builtin_fmaf(sc[r][e], scale, off[r]));
+      ps += p[e];
+    }
+    st[r].l += ps;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      pa[r].w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));
+  }
+}
+
+// The softmax half of that update for NT tiles of 16 rows that share one block: the
+// P operands of all tiles (pa), their l, and one vote for the rare rescale of O; the
+// caller then runs the P.V products, and can issue other MFMAs (the next block's
+// scores) around this vector work.  sc[r] holds tile r's raw (masked) scores.
+template <int D, int NT>
+__device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&sc)[NT][8], float scale,
+                                              Frag8 (&pa)[NT], int lane) {
+  const int c = lane >> 4;
+  bool grow[NT];
+  float mref[NT];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    float bm = sc[r][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[r][e]);
+    bm = row_max4(bm);
     grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
     mref[r] = grow[r] ? bm : st[r].m;
     any |= grow[r];
@@ -543,10 +613,6 @@ __device__ __forceinline__ void softmax_pv_tiles(State<D> (&st)[NT], const Block
       st[r].m = mref[r];
     }
   }
-#pragma unroll
-  for (int r = 0; r < NT; ++r)
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) st[r].o[dt] = mma(pa[r].v, b.v[dt], st[r].o[dt]);
 }
 
 // Blocks [b0, b1) of one (sequence, kv head), folded in order by fold(block, t0).

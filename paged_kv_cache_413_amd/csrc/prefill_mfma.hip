@@ -158,15 +158,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 }
 
 // ---- LDS-shared variant (pages of >= 32 tokens) -----------------------------------------
-// A workgroup of kPfWaves waves (two per SIMD, kPfTiles row tiles each, so that one
-// wave's softmax runs while the other's MFMAs do) shares one K/V stream: every 32-token
-// block is fetched once per workgroup -- each thread loads 64 bytes of it into
-// registers two blocks ahead (two register slots), then writes them into one of
-// two LDS stages -- and each wave reads its MFMA operands from the stage with the
-// same lane offsets as from the tile in HBM.  The stage layout mirrors the block's HBM
-// layout: K as D/32 chunks of [32 tokens][32 dims], then V as [D][32 positions].
-constexpr int kPfWaves = 8;     // two per SIMD: one's softmax overlaps the other's MFMAs
-constexpr int kPfTiles = 2;     // 16-row tiles per wave of the LDS-shared kernel
+// A workgroup of kPfWaves waves (one per SIMD, kPfTiles row tiles each) shares one K/V
+// stream: every 32-token block is fetched once per workgroup -- each thread loads its
+// 16-byte pieces of it into registers four blocks ahead (two register slots), then
+// writes them into one of three LDS stages two blocks ahead -- and each wave reads its
+// MFMA operands from the stage with the same lane offsets as from the tile in HBM.  The
+// stage layout mirrors the block's HBM layout: K as D/32 chunks of [32 tokens][32
+// dims], then V as [D][32 positions].  Three stages let a wave compute the scores of
+// block i+1 (matrix cores) while it runs the softmax of block i (vector ALU) and then
+// the P.V products of block i: the two units work at once within each wave, instead
+// of every wave waiting on one then the other between barriers.
+#ifndef PKV_PF_WAVES
+#define PKV_PF_WAVES 8
+#endif
+#ifndef PKV_PF_TILES
+#define PKV_PF_TILES 2
+#endif
+constexpr int kPfWaves = PKV_PF_WAVES;   // waves of a workgroup (a multiple of the 4 SIMDs)
+constexpr int kPfTiles = PKV_PF_TILES;   // 16-row tiles per wave of the LDS-shared kernel
+constexpr int kPfStages = 3;
+#ifndef PKV_PF_SCHED
+#define PKV_PF_SCHED 2  // vector instructions the scheduler puts after each MFMA of a step (0: its own order)
+#endif
 
 template <int KV, int D>
 struct PfStage {
@@ -204,12 +217,12 @@ __device__ __forceinline__ bf16x8 lds8(const char* p) {
 }
 
 template <int KV, int D, int G>
-__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_lds_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(kPfWaves / 4, kPfWaves / 4))) void prefill_lds_kernel(AttnArgs a) {
   using SL = PfStage<KV, D>;
   constexpr int NT = kPfTiles, QPT = PfGeom<G>::QPT, QWV = NT * QPT;
   constexpr int QWG = kPfWaves * QWV;
   constexpr int esz = SL::esz;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * SL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[kPfStages * SL::BYTES];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
   const int QT = a.pf_qtiles;
@@ -300,8 +313,38 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   // and the operand reads apply the same map.
   const uint32_t wofs = esz == 2 ? uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 3) & 3)))
                                  : uint32_t(lane * 16);
-  auto stash = [&](const uint4 (&r)[SL::PER_WAVE], int stage) {
+  // Stage a block; in the sequence's last, partial block the V slots past its end are
+  // zeroed here (they may hold anything, NaN included, and a zero weight would not
+  // cancel a NaN), so the operand reads need no tail test.  The lane's 16 bytes are
+  // positions 8(lane & 3) + e of a 32-slot row (bf16) or 16(lane & 1) + e (FP8); the
+  // token at position p of a V row is tok_of(p >> 3, p & 7).
+  auto stash = [&](uint4 (&r)[SL::PER_WAVE], int stage, int blk) {
     char* dst = smem + stage * SL::BYTES;
+    const int nvalid = L - (blk << LOG2_BT);
+    if (nvalid < BT) {  // wave-uniform, once per sequence
+#pragma unroll
+      for (int k = 0; k < SL::PER_WAVE; ++k) {
+        if (w + k * kPfWaves < SL::KPIECES) continue;
+        uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t keep = 0;
+          if constexpr (esz == 2) {
+            const int p0 = 8 * (lane & 3) + 2 * j;
+            keep = (tok_of(p0 >> 3, p0 & 7) < nvalid ? 0x0000ffffu : 0u) |
+                   (tok_of((p0 + 1) >> 3, (p0 + 1) & 7) < nvalid ? 0xffff0000u : 0u);
+          } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const int pp = 16 * (lane & 1) + 4 * j + b;
+              keep |= tok_of(pp >> 3, pp & 7) < nvalid ? (0xffu << (8 * b)) : 0u;
+            }
+          }
+          wd[j] &= keep;
+        }
+        r[k] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      }
+    }
 #pragma unroll
     for (int k = 0; k < SL::PER_WAVE; ++k) {
       if (!SL::EVEN && w + k * kPfWaves >= SL::PIECES) break;
@@ -312,11 +355,9 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
   const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3))) : uint32_t(n * 32 + 8 * c);
-  // Fold block b0+i from stage i%2 (the wave's rows only need blocks below kend_w).
-  auto compute = [&](int i) {
-    const int t = (b0 + i) << LOG2_BT;
-    if (t >= kend_w) return;
-    const char* stg = smem + (i & 1) * SL::BYTES;
+  // Raw scores of block b0+i (stage i%3) for the wave's tiles.
+  auto scores = [&](int i, float (&sc)[NT][8]) {
+    const char* stg = smem + (i % kPfStages) * SL::BYTES;
     Block<D> b;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
@@ -324,47 +365,72 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2
       b.kb[j] = lds8<KV>(stg + j * SL::KCHUNK + 16 * 32 * esz + lk);
     }
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) b.v[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
-    if (t + BT > L) mask_v_tail<D>(b, L - t, lane);
-    float sc[NT][8];
-#pragma unroll
     for (int r = 0; r < NT; ++r) block_scores<D>(b, qf[r], sc[r]);
+  };
+  // Step i: block i+2 goes from its register slot into stage (i+2)%3 -- last read (V
+  // of block i-1) before the previous step's barrier -- and the slot refills with block
+  // i+4 (clamped to the last block: a harmless repeat near the end).  Then block i is
+  // folded: its scores (cur, from the previous step) are masked where the block
+  // reaches a row's position or lies past the wave's rows (every weight there is 0,
+  // so such a block changes nothing), maxima and the rare rescale vote come first, and
+  // the main region -- exponentials of block i, the scores of block i+1 into nxt
+  // (stage (i+1)%3, complete since the previous barrier; clamped at the end), the
+  // P.V products of block i -- is one straight-line stretch in which the scheduler
+  // interleaves the matrix-core and vector instructions.
+  const int last = b1 - 1;
+  uint4 ra[SL::PER_WAVE], rb[SL::PER_WAVE];
+  float sa_[NT][8], sb_[NT][8];
+  auto step = [&](uint4 (&rs)[SL::PER_WAVE], int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
+    const int t = (b0 + i) << LOG2_BT;
+    const int blk2 = min(b0 + i + 2, last);
+    stash(rs, (i + 2) % kPfStages, blk2);
+    fetch(rs, min(b0 + i + 4, last));
     if (t + BT > lim_min) {  // wave-uniform: the block reaches some row's position
 #pragma unroll
       for (int r = 0; r < NT; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (t + tok_of(c, e) >= lim[r]) sc[r][e] = -INFINITY;
+          if (t + tok_of(c, e) >= lim[r]) cur[r][e] = -INFINITY;
     }
-    softmax_pv_tiles<D, NT>(st, b, sc, qk_scale, lane);
+    float off[NT];
+    softmax_head<D, NT>(st, cur, qk_scale, off, lane);
+    const char* stg = smem + (i % kPfStages) * SL::BYTES;
+    bf16x8 vv[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vv[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
+    Frag8 pa[NT];
+    softmax_tail<NT>(st, cur, qk_scale, off, pa);
+    scores(min(i + 1, nblk - 1), nxt);
+#pragma unroll
+    for (int r = 0; r < NT; ++r)
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) st[r].o[dt] = mma(pa[r].v, vv[dt], st[r].o[dt]);
+#if PKV_PF_SCHED
+    // exponentials and conversions of block i around the scores of block i+1
+#pragma unroll
+    for (int k = 0; k < NT * D / 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x0002, PKV_PF_SCHED, 0);  // vector ALU
+    }
+#endif
+    stage_barrier();
   };
-  // Register slots hold the next blocks: ra the even-numbered, rb the odd-numbered
-  // ones.  At step i, block i+1 goes from its slot into stage (i+1)%2 -- last read
-  // during block i-1, before the previous step's barrier -- and the slot refills with
-  // block i+3 (clamped to the last block: a harmless repeat near the end).  Stash and
-  // refill are unconditional and the slots static, so every wait is for the older
-  // slot's loads only.
-  const int last = b1 - 1;
-  uint4 ra[SL::PER_WAVE], rb[SL::PER_WAVE];
   if (nblk > 0) {
     fetch(ra, b0);
     fetch(rb, min(b0 + 1, last));
-    stash(ra, 0);
+    stash(ra, 0, b0);
     fetch(ra, min(b0 + 2, last));
+    stash(rb, 1, min(b0 + 1, last));
+    fetch(rb, min(b0 + 3, last));
     stage_barrier();
+    scores(0, sa_);
   }
   int i = 0;
   for (; i + 1 < nblk; i += 2) {
-    stash(rb, 1);                      // block i+1 (odd) -> stage 1
-    fetch(rb, min(b0 + i + 3, last));
-    compute(i);
-    stage_barrier();
-    stash(ra, 0);                      // block i+2 (even) -> stage 0
-    fetch(ra, min(b0 + i + 4, last));
-    compute(i + 1);
-    stage_barrier();
+    step(ra, i, sa_, sb_);      // slot ra holds the even blocks; scores alternate sa_/sb_
+    step(rb, i + 1, sb_, sa_);
   }
-  if (i < nblk) compute(i);
+  if (i < nblk) step(ra, i, sa_, sb_);
   if (!live) return;
   prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane);
 }
