@@ -165,7 +165,10 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
  * first).  Query i of sequence s sits at position context_lens[s] - C_s + i and
  * attends to keys 0 .. that position.
  *   q: packed [total_q][num_q_heads][head_dim] of q_dtype (F32 or BF16; BF16 with a
- *         BF16 or FP8 cache and pages of >= 8 tokens runs on the matrix cores).
+ *         BF16 or FP8 cache and pages of >= 8 tokens runs on the matrix cores; there,
+ *         chunks of at most 16 / G queries -- several tokens verified per sequence,
+ *         as in speculative decoding -- run on the balanced decode kernels, all
+ *         queries of a (sequence, kv head) sharing one pass over its keys).
  *   cu_q_lens: [num_seqs + 1] int32 prefix sums of the chunk lengths C_s, with
  *         C_s <= context_lens[s].
  *   total_q, max_q_len: HOST values (rows of q; an upper bound of C_s).

@@ -180,7 +180,7 @@ int auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
 // Workspace: partial log-sum-exps and normalised partial outputs (fp32), after one
 // 16-byte descriptor per wave for the balanced schedule.
 DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
-                       int q_dtype, int num_splits) {
+                       int q_dtype, int num_splits, int record_rows = 0) {
   const int P = c.page_size;
   const int64_t maxL = s.max_context_len;
   const int G = num_q_heads / c.num_kv_heads;
@@ -192,10 +192,11 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
     p.chunk = 0;
     p.max_splits = 0;
     const size_t recs = size_t(2) * p.waves;  // up to two cut segments per wave
+    const size_t rows = record_rows > 0 ? size_t(record_rows) : size_t(G);  // tile rows per record
     p.off_desc = 0;
     p.off_lse = align256(size_t(p.waves) * 16);
-    p.off_o = p.off_lse + align256(recs * G * sizeof(float));
-    p.ws_bytes = p.off_o + align256(recs * G * c.head_dim * sizeof(float));
+    p.off_o = p.off_lse + align256(recs * rows * sizeof(float));
+    p.ws_bytes = p.off_o + align256(recs * rows * c.head_dim * sizeof(float));
     return p;
   }
   int64_t chunk;
@@ -234,6 +235,12 @@ struct PrefillPlan {
   bool mfma;
   int qtiles, splits;
   size_t off_lse, off_o, ws_bytes;
+  // Chunks of at most 16 / G queries (speculative-verification and similar short
+  // chunks): all queries of a (sequence, kv head) fit one 16-row MFMA tile, so the call
+  // runs on the balanced decode kernels -- HBM-bound streaming of each sequence's K/V
+  // once -- instead of the query-tiled prefill kernels.
+  bool via_decode;
+  DecodePlan dec;
 };
 
 PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
@@ -242,6 +249,14 @@ PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num
   const int G = num_q_heads / c.num_kv_heads;
   p.mfma = pkv::mfma_decode_supported(c.dtype, q_dtype, c.head_dim, G, c.page_size);
   if (!p.mfma) return p;
+  if (G <= 8 && int64_t(max_q_len) * G <= 16) {
+    p.dec = plan_decode(c, s, num_q_heads, q_dtype, 0, 16);
+    if (p.dec.auto_mode) {
+      p.via_decode = true;
+      p.ws_bytes = p.dec.ws_bytes;
+      return p;
+    }
+  }
   int qw = 1, resident_items = 1;
   pkv::mfma_prefill_geometry(c.dtype, c.head_dim, G, c.page_size, &qw, &resident_items);
   p.qtiles = int(cdiv(max_q_len, qw));
@@ -343,7 +358,7 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
     a.num_waves = p.waves;
     a.min_share = kMinShareBlocks;
     a.ws_desc = p.auto_mode ? reinterpret_cast<int4*>(ws + p.off_desc) : nullptr;
-    pkv::MfmaPlan mp{p.auto_mode, p.waves};
+    pkv::MfmaPlan mp{p.auto_mode, p.waves, false};
     return launch_status(pkv::launch_mfma_decode(a, mp, hs), "paged_attn_decode");
   }
   return launch_status(pkv::launch_valu_decode(a, hs), "paged_attn_decode");
@@ -393,6 +408,16 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
   a.total_q = total_q;
   a.max_q_len = max_q_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.via_decode) {
+    char* ws = static_cast<char*>(workspace);
+    a.ws_lse = reinterpret_cast<float*>(ws + p.dec.off_lse);
+    a.ws_o = reinterpret_cast<float*>(ws + p.dec.off_o);
+    a.ws_desc = reinterpret_cast<int4*>(ws + p.dec.off_desc);
+    a.num_waves = p.dec.waves;
+    a.min_share = kMinShareBlocks;
+    pkv::MfmaPlan mp{true, p.dec.waves, true};
+    return launch_status(pkv::launch_mfma_decode(a, mp, hs), "paged_attn_prefill_chunk");
+  }
   if (p.mfma) {
     char* ws = static_cast<char*>(workspace);
     a.max_splits = p.splits;

@@ -38,20 +38,23 @@
 namespace pkv {
 namespace {
 
-// Fold one block into the state of the G heads (the MFMA rows; unused rows are zero).
-// t_end: first token past this range; when the block reaches past it (the range's
-// last block) the excess tokens' scores are masked and their V entries zeroed.
+// Fold one block into the state of the tile's rows.  t_end: first token past this
+// range; lim_row: this lane's row sees keys t < lim_row (its causal limit: the sequence
+// length for decode); lim_min = min(t_end, smallest lim_row), wave-uniform.  On the
+// blocks that reach it the excess keys' scores are masked, and on the range's last,
+// partial block the V entries past t_end are zeroed.
 template <int D>
 __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16x8 (&qf)[D / 32],
-                                           float qk_scale, int t, int t_end, int lane) {
+                                           float qk_scale, int t, int t_end, int lim_row, int lim_min,
+                                           int lane) {
   float sc[8];
   block_scores<D>(b, qf, sc);
-  if (t + BT > t_end) {  // wave-uniform: the range's last, partial block
-    const int c = lane >> 4, nvalid = t_end - t;
+  if (t + BT > lim_min) {  // wave-uniform
+    const int c = lane >> 4, lim = min(t_end, lim_row);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (tok_of(c, e) >= nvalid) sc[e] = -INFINITY;
-    mask_v_tail<D>(b, nvalid, lane);
+      if (t + tok_of(c, e) >= lim) sc[e] = -INFINITY;
+    if (t + BT > t_end) mask_v_tail<D>(b, t_end - t, lane);
   }
   softmax_pv<D>(st, b, sc, qk_scale, lane);
 }
@@ -60,25 +63,28 @@ __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
-                                          int b0, int b1, int t_end, int L, int log2P,
+                                          int b0, int b1, int t_end, int lim_row, int lim_min, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane,
-                            [&](Block<D>& b, int t) { fold_block<D>(st, b, qf, qk_scale, t, t_end, lane); });
+  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](Block<D>& b, int t) {
+    fold_block<D>(st, b, qf, qk_scale, t, t_end, lim_row, lim_min, lane);
+  });
 }
 
-// Finish a range: reduce the running sum over the four lane groups of each head and
-// normalise.  A range that covers its whole (query row, kv head) writes the output
-// (bf16) and log-sum-exp directly; a cut one writes partial record `rec`:
-// ws_o[rec][G][D] (normalised) and ws_lse[rec][G], merged by the merge kernel.
-template <int D, int G>
-__device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, int row, int g,
+// Finish a range: reduce the running sum over the four lane groups of each row and
+// normalise.  Tile row R is query R / G of the sequence (packed row q0 + R / G) and
+// head g*G + R % G; rows of queries >= nq are not written.  A range that covers its
+// whole (sequence, kv head) writes the output (bf16) and log-sum-exp directly; a cut
+// one writes partial record `rec`: ws_o[rec][ROWS][D] (normalised) and
+// ws_lse[rec][ROWS], merged by the merge kernel.
+template <int D, int G, int ROWS>
+__device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, int q0, int nq, int g,
                                        bool complete, int64_t rec, float qk_scale, float vscale,
                                        int lane) {
   const int nn = lane & 15, c = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const float lse = row_lse(st.m, l, qk_scale);  // natural log, valid in lanes nn < G
+  const float lse = row_lse(st.m, l, qk_scale);  // natural log of row nn
   float inv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -90,26 +96,27 @@ __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, in
     uint16_t* out = static_cast<uint16_t*>(a.out);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int h = 4 * c + i;
-      if (h < G) {
-        uint16_t* o = out + (int64_t(row) * Hq + g * G + h) * D + nn;
+      const int R = 4 * c + i;
+      if (R < ROWS && R / G < nq) {
+        uint16_t* o = out + (int64_t(q0 + R / G) * Hq + g * G + R % G) * D + nn;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = uint16_t(f32_to_bf16(st.o[dt][i] * inv[i]));
       }
     }
-    if (a.lse_out && c == 0 && nn < G) a.lse_out[int64_t(row) * Hq + g * G + nn] = lse;
+    if (a.lse_out && c == 0 && nn < ROWS && nn / G < nq)
+      a.lse_out[int64_t(q0 + nn / G) * Hq + g * G + nn % G] = lse;
     return;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * c + i;
-    if (h < G) {
-      float* o = a.ws_o + (rec * G + h) * D + nn;
+    const int R = 4 * c + i;
+    if (R < ROWS) {
+      float* o = a.ws_o + (rec * ROWS + R) * D + nn;
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) o[16 * dt] = st.o[dt][i] * inv[i];
     }
   }
-  if (c == 0 && nn < G) a.ws_lse[rec * G + nn] = lse;
+  if (c == 0 && nn < ROWS) a.ws_lse[rec * ROWS + nn] = lse;
 }
 
 // Independent waves per workgroup of the decode kernels (no LDS, no barriers: a larger
@@ -139,16 +146,16 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   float qk_scale, vscale;
   scales<KV>(a, g, qk_scale, vscale);
   bf16x8 qf[D / 32];
-  load_q<D, G>(qf, a.q, s, a.num_q_heads, g, lane);
+  load_q<D, G>(qf, a.q, s, 1, a.num_q_heads, g, lane);
   State<D> st;
   state_init(st);
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
   const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
   run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt,
-                           t0 >> LOG2_BT, (t1 + BT - 1) >> LOG2_BT, t1, L, a.cache.log2_page,
+                           t0 >> LOG2_BT, (t1 + BT - 1) >> LOG2_BT, t1, L, t1, L, a.cache.log2_page,
                            Hkv * tile_b, g * tile_b, lane);
-  finish<D, G>(st, a, s, g, nsplit == 1, int64_t(sg) * a.max_splits + split, qk_scale, vscale, lane);
+  finish<D, G, G>(st, a, s, 1, g, nsplit == 1, int64_t(sg) * a.max_splits + split, qk_scale, vscale, lane);
 }
 
 // ---- auto: contiguous equal shares of the flattened block space ------------------------
@@ -195,8 +202,13 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, int S, 
   cum_out = run;
 }
 
-template <int KV, int D, int G, bool SMALLP>
+// MQ (several queries per sequence: prefill chunks of at most 16 / G queries): the
+// tile's rows are (query, head) pairs, query j of sequence s is packed row
+// cu_q_lens[s] + j at position L - nq + j, and records hold 16 rows.  Otherwise one
+// query per sequence (packed row s) and records of G rows.
+template <int KV, int D, int G, bool SMALLP, bool MQ>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
+  constexpr int ROWS = MQ ? 16 : G;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWgWaves + (threadIdx.x >> 6);
   if (w >= a.num_waves) return;
@@ -236,16 +248,20 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
     }
     float qk_scale, vscale;
     scales<KV>(a, g, qk_scale, vscale);
+    const int q0 = MQ ? a.cu_q_lens[s] : s;
+    const int nq = MQ ? a.cu_q_lens[s + 1] - q0 : 1;
     bf16x8 qf[D / 32];
-    load_q<D, G>(qf, a.q, s, a.num_q_heads, g, lane);
+    load_q<D, G>(qf, a.q, q0, nq, a.num_q_heads, g, lane);
     State<D> st;
     state_init(st);
     const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
     const int t_end = min(L, b1 << LOG2_BT);
+    const int lim_row = L - nq + (lane & 15) / G + 1;  // causal limit of this lane's row
     run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, b0, b1,
-                             t_end, L, a.cache.log2_page, Hkv * tile_b, g * tile_b, lane);
+                             t_end, lim_row, min(t_end, L - nq + 1), L, a.cache.log2_page, Hkv * tile_b,
+                             g * tile_b, lane);
     const bool complete = b0 == 0 && b1 == nb;
-    finish<D, G>(st, a, s, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
+    finish<D, G, ROWS>(st, a, q0, nq, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
     first = false;
     f = gs + b1;
     if (g + 1 == Hkv) {
@@ -266,14 +282,16 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
 #endif
 constexpr int kAutoMergeThreads = PKV_AUTO_MERGE_THREADS;
 
-template <int D, int G>
+template <int D, int G, bool MQ>
 __global__ __launch_bounds__(kAutoMergeThreads) void merge_auto_kernel(AttnArgs a) {
   const int w = blockIdx.x;
   const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
   if (d.x < 0 || !(d.w & 1)) return;
   const int w0 = d.z;
   const bool slot1 = d.w & 2;
-  merge_partials<D, G, kAutoMergeThreads>(a, d.x, d.y, w - w0 + 1, [w0, slot1](int i) {
+  const int q0 = MQ ? a.cu_q_lens[d.x] : d.x;
+  const int nq = MQ ? a.cu_q_lens[d.x + 1] - q0 : 1;
+  merge_partials<D, G, MQ ? 16 : G, kAutoMergeThreads>(a, q0, nq, d.y, w - w0 + 1, [w0, slot1](int i) {
     return int64_t(w0 + i) * 2 + ((i == 0 && slot1) ? 1 : 0);
   });
 }
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) 
   const int n = (a.seqs.context_lens[s] + a.chunk - 1) / a.chunk;
   if (n <= 1) return;  // written directly
   const int64_t r0 = int64_t(sg) * a.max_splits;
-  merge_partials<D, G, kMergeThreads>(a, s, g, n, [r0](int i) { return r0 + i; });
+  merge_partials<D, G, G, kMergeThreads>(a, s, 1, g, n, [r0](int i) { return r0 + i; });
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -295,11 +313,21 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) 
 template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
   if (p.auto_mode) {
-    hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP>), dim3(unsigned((p.waves + kWgWaves - 1) / kWgWaves)),
-                       dim3(64 * kWgWaves), 0, st, a);
+    const dim3 grid(unsigned((p.waves + kWgWaves - 1) / kWgWaves)), block(64 * kWgWaves);
+    if (p.multi_query) {
+      if constexpr (G <= 8) {  // 16 / G >= 2 queries per tile
+        hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP, true>), grid, block, 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((merge_auto_kernel<D, G, true>), dim3(p.waves), dim3(kAutoMergeThreads), 0, st, a);
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP, false>), grid, block, 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_auto_kernel<D, G>), dim3(p.waves), dim3(kAutoMergeThreads), 0, st, a);
+    hipLaunchKernelGGL((merge_auto_kernel<D, G, false>), dim3(p.waves), dim3(kAutoMergeThreads), 0, st, a);
     return hipGetLastError();
   }
   const int64_t nblk = int64_t(a.seqs.num_seqs) * a.cache.num_kv_heads * a.max_splits;
@@ -338,8 +366,8 @@ hipError_t dispatch_d(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
 // representative: G only changes which MFMA rows are used).
 template <int KV, int D>
 const void* auto_kernel_for(int G, bool smallp) {
-#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, true>) \
-                          : reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, false>))
+#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, true, false>) \
+                          : reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, false, false>))
   switch (G) {
     case 1: return PKV_K(1);
     case 2: return PKV_K(2);

@@ -64,8 +64,10 @@ hipError_t launch_valu_prefill(const AttnArgs& a, hipStream_t stream);
 // Matrix-core decode kernels (attn_mfma.hip): bf16 / FP8 caches with bf16 queries,
 // page sizes >= 8, groups of up to 16 query heads per kv head.
 struct MfmaPlan {
-  bool auto_mode;  // true: balanced shares over `waves`; false: fixed partitions
+  bool auto_mode;    // true: balanced shares over `waves`; false: fixed partitions
   int waves;
+  bool multi_query;  // auto only: several queries per sequence (prefill chunks of at most
+                     // 16 / G queries, packed by cu_q_lens), 16-row partial records
 };
 bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, int page_size);
 int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size);

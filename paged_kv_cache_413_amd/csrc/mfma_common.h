@@ -282,14 +282,16 @@ __device__ __forceinline__ float row_lse(float m, float l, float scale) {
   return l > 0.f ? (m * scale + __log2f(l)) * kLn2 : -INFINITY;
 }
 
-// Q^T operand of query row `row`, kv head g: lane (n, c) holds dims 32j + 8c .. +7 of
-// query head g*G + n (zero for n >= G).  Queries are bf16.
+// Q^T operand of a 16-row tile for kv head g: tile row n = (query j = n / G, head
+// g*G + n % G); lane (n, c) holds dims 32i + 8c .. +7 of that query head, zero for rows
+// with j >= nq (the sequence's queries in this call; 1 for decode).  q0 = packed row of
+// the sequence's query 0.  Queries are bf16.
 template <int D, int G>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restrict__ q, int row,
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restrict__ q, int q0, int nq,
                                        int Hq, int g, int lane) {
   const int n = lane & 15, c = lane >> 4;
-  if (n < G) {
-    const uint16_t* base = static_cast<const uint16_t*>(q) + (int64_t(row) * Hq + g * G + n) * D + 8 * c;
+  if (n / G < nq) {
+    const uint16_t* base = static_cast<const uint16_t*>(q) + (int64_t(q0 + n / G) * Hq + g * G + n % G) * D + 8 * c;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
       Frag8 f;
@@ -302,19 +304,20 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restr
   }
 }
 
-// Merge the n partial records of one (query row, kv head) -- record i is rec(i) --
+// Merge the n partial records of one (sequence, kv head) -- record i is rec(i) --
 // into the final output and log-sum-exp: LSE_h = log sum_i exp(lse_ih),
-// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  One workgroup of NT threads: every thread
-// owns float4 chunks of the G x D record (one head each) and a stride of records,
-// and keeps a running (max, sum of weights, weighted sum) over them, so the loads
-// of different records are independent and in flight together; the record-parallel
-// states are then combined in LDS.  Every thread of the workgroup must call it (it
-// may hold barriers); it may be called repeatedly.
+// out_h = sum_i exp(lse_ih - LSE_h) o_ih.  A record holds ROWS tile rows (row R = query
+// R / G of the sequence, head g*G + R % G; rows of queries >= nq are skipped) x D.
+// One workgroup of NT threads: every thread owns float4 chunks of the record (one row
+// each) and a stride of records, and keeps a running (max, sum of weights, weighted
+// sum) over them, so the loads of different records are independent and in flight
+// together; the record-parallel states are then combined in LDS.  Every thread of the
+// workgroup must call it (it may hold barriers); it may be called repeatedly.
 constexpr int kMergeThreads = 256;
 
-template <int D, int G, int NT, typename RecFn>
-__device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g, int n, RecFn rec) {
-  constexpr int C = G * D / 4;                  // float4 chunks per record
+template <int D, int G, int ROWS, int NT, typename RecFn>
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int q0, int nq, int g, int n, RecFn rec) {
+  constexpr int C = ROWS * D / 4;               // float4 chunks per record
   constexpr int CC = C < NT ? C : NT;           // chunk lanes
   constexpr int RP = NT / CC;                   // record-parallel factor
   constexpr int CPT = (C + NT - 1) / NT;        // chunks per thread
@@ -334,9 +337,9 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int e = (cl + k * CC) * 4;
-      if (e < G * D) {
-        const float x = a.ws_lse[r * G + e / D];
-        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + r * (G * D) + e);
+      if (e < ROWS * D && (e / D) / G < nq) {
+        const float x = a.ws_lse[r * ROWS + e / D];
+        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + r * (ROWS * D) + e);
         if (x == -INFINITY) continue;  // a piece that saw no key of this row
         const float mn = fmaxf(m[k], x);
         const float sa = __expf(m[k] - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
@@ -383,14 +386,16 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int row, int g
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int e = (cl + k * CC) * 4;
-      if (e < G * D) {
-        const int h = e / D, d = e % D;
+      const int R = e / D;
+      if (e < ROWS * D && R / G < nq) {
+        const int d = e % D;
+        const int64_t row = int64_t(q0 + R / G) * a.num_q_heads + g * G + R % G;
         const float inv = 1.f / w[k];
-        uint16_t* o = static_cast<uint16_t*>(a.out) + (int64_t(row) * a.num_q_heads + g * G + h) * D + d;
+        uint16_t* o = static_cast<uint16_t*>(a.out) + row * D + d;
         const uint32_t lo = f32_to_bf16(acc[k].x * inv) | (f32_to_bf16(acc[k].y * inv) << 16);
         const uint32_t hi = f32_to_bf16(acc[k].z * inv) | (f32_to_bf16(acc[k].w * inv) << 16);
         *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
-        if (a.lse_out && d == 0) a.lse_out[int64_t(row) * a.num_q_heads + g * G + h] = m[k] + __logf(w[k]);
+        if (a.lse_out && d == 0) a.lse_out[row] = m[k] + __logf(w[k]);
       }
     }
   }

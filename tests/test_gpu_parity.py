@@ -248,6 +248,46 @@ def test_auto_decode_few_waves(gpu_lib, monkeypatch, waves, cfg, over):
     assert torch.equal(first[1].view(torch.int32), db.lse_dec.view(torch.int32))
 
 
+SHORT_CHUNKS = [
+    # (waves (0 = device), page_size, chunks, cached, num_q_heads, num_kv_heads, head_dim):
+    # chunks of at most 16 / G queries run on the balanced decode kernels
+    (0, 64, [1, 2, 3, 4, 4, 2, 1], [100, 700, 2000, 64, 33, 4000, 5], 32, 8, 128),   # G = 4
+    (0, 16, [2, 1, 2], [300, 17, 1000], 64, 8, 128),                              # G = 8, pages of 16
+    (0, 32, [8, 5, 1, 7], [40, 300, 1200, 0], 16, 8, 64),                          # G = 2, D = 64
+    (0, 128, [16, 3, 9], [129, 500, 31], 8, 8, 128),                               # G = 1, 16 queries
+    (7, 64, [4, 4, 3, 1, 2], [3000, 800, 64, 1500, 90], 32, 8, 128),               # few waves: cut segments
+]
+
+
+@pytest.mark.parametrize("waves,P,chunks,cached,hq,hkv,D", SHORT_CHUNKS)
+def test_short_chunks_via_decode_kernels(gpu_lib, monkeypatch, waves, P, chunks, cached, hq, hkv, D):
+    """Prefill chunks of at most 16 / G queries (several tokens verified per sequence,
+    as in speculative decoding) through paged_attn_prefill_chunk: all queries of a
+    (sequence, kv head) share one MFMA tile of the decode kernels, each row with its
+    causal limit; ragged chunk lengths, cut segments, every G that allows two or more
+    queries per tile."""
+    from paged_kv_cache_413_amd import binding as B
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    if waves:
+        monkeypatch.setenv("PKV_AUTO_WAVES", str(waves))
+    wl = workloads.make(3, num_seqs=0, num_prefill=len(chunks), prefill_chunk=chunks, prefill_cached=cached,
+                        page_size=P, num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
+    print(f"[case] short chunks waves={waves} P={P} chunks={chunks} Hq={hq} Hkv={hkv} D={D}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.prepare_step()
+    # the decode-kernel plan: its workspace is the balanced decode schedule's, with
+    # 16-row records (differs from the query-tiled prefill plan's)
+    ws = B.paged_attn_prefill_workspace_size(db.cache, db.seqs_pf, db.q_code, hq, db.npf_q, db.max_q)
+    assert ws > 0
+    db.step()
+    torch.cuda.synchronize()
+    _, _, pf, pf_lse = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(pf, ref[2], "bf16", f"chunks={chunks}")
+    assert_lse_close(pf_lse, ref[3], "bf16", f"chunks={chunks}")
+
+
 PREFILL_EDGES = [
     # (page_size, chunks, cached, num_q_heads, num_kv_heads, head_dim)
     (64, [1, 15, 16, 17], [0, 0, 5, 100], 32, 8, 128),       # first chunks: triangular
