@@ -39,6 +39,7 @@ WORKLOADS = {
     "mixed_inflight_bf16": 3,
     "long_context_splitkv_bf16": 4,
     "fp8_shared_prefix_decode": 5,
+    "spec_verify4_bf16": 6,
 }
 # sources of the decode call on the matrix-core path (the traffic record is void once any changes)
 KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp")
@@ -69,19 +70,27 @@ def recorded_traffic(workload: str):
     return float(m_val.group(1))
 
 
+def attention_rows(wl):
+    """Sequences whose attention the measured call computes: the decode sequences, or,
+    in a workload of prefill chunks only (multi-token decode), all of them."""
+    import numpy as np
+    npf = wl.num_prefill
+    return np.arange(npf, wl.num_seqs) if npf < wl.num_seqs else np.arange(wl.num_seqs)
+
+
 def algorithmic_bytes(wl) -> dict:
-    """Bytes one decode launch must move at minimum: K and V of every attended token
-    (once per sequence), the queries and outputs, the block-table entries the
-    sequences use and their lengths."""
+    """Bytes one launch of the measured attention call must move at minimum: K and V of
+    every attended token (once per sequence), the queries and outputs, the block-table
+    entries the sequences use and their lengths."""
     import numpy as np
     elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
     qel = 4 if wl.q_dtype == "f32" else 2
-    npf = wl.num_prefill
-    L = wl.context_lens[npf:].astype(np.int64)
-    S = len(L)
+    rows = attention_rows(wl)
+    L = wl.context_lens[rows].astype(np.int64)
+    nq = int(wl.new_lens[rows].sum())
     kv = int(L.sum()) * 2 * wl.num_kv_heads * wl.head_dim * elem
-    qo = 2 * S * wl.num_q_heads * wl.head_dim * qel
-    bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + S * 4
+    qo = 2 * nq * wl.num_q_heads * wl.head_dim * qel
+    bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + len(rows) * 4
     return {"kv": kv, "total": kv + qo + bt}
 
 
@@ -94,7 +103,8 @@ def cpu_baseline(wl, budget_s: float):
 
     threads = len(os.sched_getaffinity(0))
     npf = wl.num_prefill
-    order = list(range(npf, wl.num_seqs))
+    order = attention_rows(wl).tolist()
+    prefill_only = npf == wl.num_seqs
     scales = wl.fp8_scales() if wl.kv_dtype == "fp8" else (None, None, None, None)
     ks, vs, kinv, vinv = scales
     _, poison = _fill(wl)
@@ -122,8 +132,12 @@ def cpu_baseline(wl, budget_s: float):
         t0 = time.perf_counter()
         oracle.append(pool, table, wl.context_lens[rows], wl.new_lens[rows],
                       k_new, v_new, wl.in_dtype, wl.kv_dtype, kinv, vinv)
-        oracle.decode(pool, table, wl.context_lens[rows], q, wl.q_dtype,
-                      wl.sm_scale, wl.kv_dtype, ks, vs)
+        if prefill_only:
+            oracle.prefill_chunk(pool, table, wl.context_lens[rows], np.array([0, n]), q, wl.q_dtype,
+                                 wl.sm_scale, wl.kv_dtype, ks, vs)
+        else:
+            oracle.decode(pool, table, wl.context_lens[rows], q, wl.q_dtype,
+                          wl.sm_scale, wl.kv_dtype, ks, vs)
         t_spent += time.perf_counter() - t0
         done.append(s)
         bytes_done += L * 2 * wl.num_kv_heads * wl.head_dim * elem
@@ -132,9 +146,10 @@ def cpu_baseline(wl, budget_s: float):
             break
     gbs = bytes_done / t_spent / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{len(done)} of {wl.num_seqs - npf} decode sequences of {wl.name} "
-                       f"({bytes_done / 1e6:.1f} MB of KV, {t_spent:.1f} s): kv_append of the "
-                       f"step's token then fp64 decode attention, history preloaded untimed"),
+            "sample": (f"{len(done)} of {len(order)} {'chunk' if prefill_only else 'decode'} sequences of "
+                       f"{wl.name} ({bytes_done / 1e6:.1f} MB of KV, {t_spent:.1f} s): kv_append of the "
+                       f"step's tokens then fp64 {'causal chunk' if prefill_only else 'decode'} attention, "
+                       f"history preloaded untimed"),
             "seconds": round(t_spent, 3)}
 
 
@@ -225,16 +240,19 @@ def main():
 
     append_us = per_call_us(db.append_step)
     prefill_us = per_call_us(db.prefill_step) if wl.num_prefill else None
-    decode_us = per_call_us(db.decode_step)
-    decode_ms = decode_us * 1e-3
+    decode_us = per_call_us(db.decode_step) if wl.num_prefill < wl.num_seqs else None
+    fmt = lambda us: "-" if us is None else f"{us:.1f} us"
     print(f"[bench] step {ms_step * 1e3:.1f} us; per call: append {append_us:.1f} us, prefill "
-          f"{'-' if prefill_us is None else f'{prefill_us:.1f} us'}, decode {decode_us:.1f} us",
-          file=sys.stderr, flush=True)
+          f"{fmt(prefill_us)}, decode {fmt(decode_us)}", file=sys.stderr, flush=True)
 
     ab = algorithmic_bytes(wl)
     tokens = int(wl.new_lens.sum())
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
-    achieved = ab["total"] / (decode_ms * 1e-3) / 1e9
+    # the measured attention call: decode, or the prefill call of a chunks-only workload
+    prefill_only = wl.num_prefill == wl.num_seqs
+    call = "paged_attn_prefill_chunk" if prefill_only else "paged_attn_decode"
+    call_us = prefill_us if prefill_only else decode_us
+    achieved = ab["total"] / (call_us * 1e-6) / 1e9
     traffic = recorded_traffic(wl.name)
 
     # one decode launch through the split count the bench used, for the record
@@ -262,8 +280,8 @@ def main():
         "kv_bytes": ab["kv"],
         "kernel_us": {"kv_append": round(append_us, 2),
                       "paged_attn_prefill_chunk": None if prefill_us is None else round(prefill_us, 2),
-                      "paged_attn_decode": round(decode_us, 2)},
-        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode",
+                      "paged_attn_decode": None if decode_us is None else round(decode_us, 2)},
+        "roofline": {"bound": "hbm", "kernel": call,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab["total"]},

@@ -15,10 +15,10 @@ from tests.oracle_state import oracle_sequence
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {1: 4, 2: 6, 3: 6, 4: 2, 5: 6}
+SAMPLES = {1: 4, 2: 6, 3: 6, 4: 2, 5: 6, 6: 6}
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_full_size_sampled_rows(gpu_lib, cfg):
     from paged_kv_cache_413_amd.device_batch import DeviceBatch
     wl = workloads.make(cfg)
@@ -33,7 +33,7 @@ def test_full_size_sampled_rows(gpu_lib, cfg):
     torch.cuda.empty_cache()
     npf = wl.num_prefill
     lens = wl.context_lens[npf:]
-    picks = {npf + int(np.argmin(lens)), npf + int(np.argmax(lens))}
+    picks = {npf + int(np.argmin(lens)), npf + int(np.argmax(lens))} if len(lens) else set()
     rng = np.random.default_rng(cfg)
     while len(picks) < min(SAMPLES[cfg], wl.num_seqs - npf):
         picks.add(int(rng.integers(npf, wl.num_seqs)))
@@ -43,8 +43,9 @@ def test_full_size_sampled_rows(gpu_lib, cfg):
         assert_close(dec[r:r + 1], ref_o, wl.kv_dtype, f"{wl.name} seq {s}")
         assert_lse_close(dec_lse[r:r + 1], ref_l, wl.kv_dtype, f"{wl.name} seq {s}")
     cu = wl.cu(wl.new_lens)
-    for s in range(npf):
+    pf_picks = range(npf) if npf <= 8 else sorted(set(np.random.default_rng(cfg + 100).integers(0, npf, 6).tolist()))
+    for s in pf_picks:
         ref_o, ref_l = oracle_sequence(wl, s)
         assert_close(pf[cu[s]:cu[s + 1]], ref_o, wl.kv_dtype, f"{wl.name} prefill {s}")
         assert_lse_close(pf_lse[cu[s]:cu[s + 1]], ref_l, wl.kv_dtype, f"{wl.name} prefill {s}")
-    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {npf} prefill requests", flush=True)
+    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {len(pf_picks)} prefill requests", flush=True)

@@ -320,3 +320,44 @@ def test_prefill_edge_shapes(gpu_lib, P, chunks, cached, hq, hkv, D):
     assert_close(pf, ref[2], "bf16", f"prefill P={P}")
     assert_lse_close(pf_lse, ref[3], "bf16", f"prefill P={P}")
     assert_close(dec, ref[0], "bf16", f"decode P={P}")
+
+
+@pytest.mark.parametrize("chunks", [[70, 9], [2, 4, 1]])
+def test_step_replays_from_a_captured_graph(gpu_lib, chunks):
+    """A whole step (kv_append, prefill-chunk attention, decode attention and their
+    merges) captured in a HIP graph and replayed three times, with eager kernels that
+    overwrite every output in between: each replay reproduces the eager results bit for
+    bit (the library allocates nothing and enqueues no memset, so the step captures
+    as is).  Query-tiled prefill chunks and short chunks on the decode kernels."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(3, num_seqs=6, num_prefill=len(chunks), prefill_chunk=chunks,
+                        prefill_cached=[190, 40, 700][:len(chunks)], median=300, clip=(1, 900))
+    print(f"[case] graph replay chunks={chunks}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.prepare_step()
+    outs = [db.out_dec, db.lse_dec, db.out_pf, db.lse_pf]
+    bits = lambda t: t.view(torch.int16) if t.dtype != torch.float32 else t.view(torch.int32)
+    db.step()
+    torch.cuda.synchronize()
+    eager = [bits(t).clone() for t in outs]
+    pool_eager = db.pool.view(torch.int16).clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        db.step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        db.step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, t, e in zip(("decode out", "decode lse", "prefill out", "prefill lse"), outs, eager):
+            assert torch.equal(bits(t), e), f"replay {rep}: {name}"
+        assert torch.equal(db.pool.view(torch.int16), pool_eager), f"replay {rep}: pool"

@@ -6,7 +6,7 @@ import pytest
 import workloads
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5, 6])
 def test_reproducible(cfg):
     a, b = workloads.make(cfg), workloads.make(cfg)
     assert np.array_equal(a.context_lens, b.context_lens)
@@ -33,9 +33,12 @@ def test_shapes_and_ranges():
     w5 = workloads.make(5)
     assert w5.kv_dtype == "fp8" and w5.group_size == 8
     assert w5.context_lens.min() >= 2049 and w5.context_lens.max() <= 8192
+    w6 = workloads.make(6)
+    assert w6.num_seqs == w6.num_prefill == 64 and (w6.new_lens == 4).all()
+    assert w6.context_lens.min() >= 512 and w6.context_lens.max() <= 4096 and w6.group_size == 4
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_block_tables_are_valid_assignments(cfg):
     wl = workloads.make(cfg)
     bt = wl.block_tables

@@ -321,11 +321,29 @@ def _cdiv(a, b):
 
 
 def make(cfg: int, **over) -> Workload:
-    """Build workload `cfg` (1..5).  Keyword overrides shrink it for fast tests:
+    """Build workload `cfg` (1..6).  Keyword overrides shrink it for fast tests:
     num_seqs, len_range, num_prefill, prefill_chunk, prefill_cached, context_len,
-    prefix_len, group_size, num_splits."""
-    builders = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+    prefix_len, group_size, num_splits, tokens."""
+    builders = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5, 6: _cfg6}
     return builders[cfg](**over)
+
+
+def _cfg6(**o):
+    """Multi-token decode (the speculative-verification shape), bf16: the Llama-3-8B
+    batch of workload 2 -- 64 sequences, context lengths U[512,4096] counting this
+    step's tokens, 32/8 heads, D=128, page 64 -- with `tokens` (4) new tokens per
+    sequence appended and attended causally as prefill chunks in one call.  Overrides:
+    num_seqs, len_range, tokens."""
+    S = o.get("num_seqs", 64)
+    lo, hi = o.get("len_range", (512, 4096))
+    T = o.get("tokens", 4)
+    L = _uniform_lens(6, S, lo, hi)
+    P = 64
+    pps = _cdiv(L, P)
+    npages = _pool_for(pps)
+    bt = _assign_pages(6, pps, npages)
+    return Workload("spec_verify4_bf16" if T == 4 else f"spec_verify{T}_bf16", 6, 32, 8, 128, P, "bf16",
+                    "bf16", npages, L, np.full_like(L, T), bt, num_prefill=S, num_splits=0)
 
 
 def _cfg1(**o):
