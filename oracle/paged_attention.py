@@ -92,10 +92,11 @@ def append(pool, block_tables, context_lens, new_lens, k_new, v_new, in_dtype, k
     return written
 
 
-def gather(pool, block_table_row, L: int, g: int, kv_dtype: str, k_scale=None, v_scale=None):
-    """K, V of tokens 0..L-1 of one sequence and kv head g, as float64 [L][D]."""
+def gather(pool, block_table_row, L: int, g: int, kv_dtype: str, k_scale=None, v_scale=None,
+           start: int = 0):
+    """K, V of tokens start..L-1 of one sequence and kv head g, as float64 [L-start][D]."""
     P = pool.shape[3]
-    t = np.arange(L)
+    t = np.arange(start, L)
     pages = block_table_row[t // P]
     slots = t % P
     kb = pool[pages, 0, g, slots, :]
@@ -106,15 +107,17 @@ def gather(pool, block_table_row, L: int, g: int, kv_dtype: str, k_scale=None, v
     return to_f64(kb, kv_dtype), to_f64(vb, kv_dtype)
 
 
-def attend_rows(q_rows, K, V, scale, limits=None, return_weights=False):
+def attend_rows(q_rows, K, V, scale, limits=None, return_weights=False, lower=None):
     """Softmax attention of query rows [R][D] over keys/values [L][D] in float64.
 
-    Row r attends to keys t < limits[r] (all keys when limits is None).  Returns
+    Row r attends to keys lower[r] <= t < limits[r] (no bound where None).  Returns
     (out [R][D], lse [R]) and, on request, the weights [R][L]."""
     z = np.float64(scale) * (q_rows @ K.T)
+    t = np.arange(K.shape[0])
     if limits is not None:
-        t = np.arange(K.shape[0])
         z = np.where(t[None, :] < np.asarray(limits)[:, None], z, -np.inf)
+    if lower is not None:
+        z = np.where(t[None, :] >= np.asarray(lower)[:, None], z, -np.inf)
     m = z.max(axis=1)
     e = np.exp(z - m[:, None])
     lsum = e.sum(axis=1)
@@ -126,12 +129,22 @@ def attend_rows(q_rows, K, V, scale, limits=None, return_weights=False):
     return out, lse
 
 
+def window_start(pos: int, window: int) -> int:
+    """First key a query at position `pos` attends to: 0, or with a limited attention
+    window of W tokens the W newest positions up to and including its own, keys
+    pos - W + 1 .. pos ([Deep dive] §11: tokens outside a sliding window take no
+    further part in attention; the pages leave the boundary open and this is the
+    plainest reading)."""
+    return max(0, pos - window + 1) if window > 0 else 0
+
+
 def decode(pool, block_tables, context_lens, q, q_dtype, sm_scale, kv_dtype,
-           k_scale=None, v_scale=None, return_weights=False):
+           k_scale=None, v_scale=None, return_weights=False, window=0):
     """One decode step's attention: every query head of sequence s attends to all
     context_lens[s] tokens in the cache, the token appended this step included
     ([Deep dive] §2: a decode step reads the whole history; appending first means
-    the new token attends to itself, as in causal attention).
+    the new token attends to itself, as in causal attention) -- or, with a window W,
+    to the last W of them.
 
     q is [S][Hq][D] in q_dtype; returns (out [S][Hq][D], lse [S][Hq]) float64."""
     S, Hq, D = q.shape
@@ -142,8 +155,9 @@ def decode(pool, block_tables, context_lens, q, q_dtype, sm_scale, kv_dtype,
     weights = {}
     for s in range(S):
         L = int(context_lens[s])
+        lo = window_start(L - 1, window)
         for g in range(Hkv):
-            K, V = gather(pool, block_tables[s], L, g, kv_dtype, k_scale, v_scale)
+            K, V = gather(pool, block_tables[s], L, g, kv_dtype, k_scale, v_scale, start=lo)
             rows = to_f64(q[s, g * G:(g + 1) * G], q_dtype)
             res = attend_rows(rows, K, V, np.float32(sm_scale), None, return_weights)
             out[s, g * G:(g + 1) * G] = res[0]
@@ -156,14 +170,15 @@ def decode(pool, block_tables, context_lens, q, q_dtype, sm_scale, kv_dtype,
 
 
 def prefill_chunk(pool, block_tables, context_lens, cu_q_lens, q, q_dtype, sm_scale,
-                  kv_dtype, k_scale=None, v_scale=None):
+                  kv_dtype, k_scale=None, v_scale=None, window=0):
     """Causal attention of a prefill chunk against the cache it was just appended to.
 
     Sequence s has C = cu_q_lens[s+1] - cu_q_lens[s] query tokens; query i sits at
     position p = context_lens[s] - C + i and attends to keys 0..p ([Deep dive] §8:
     a long prompt is cut into chunks, each chunk adds its KV to the cache and later
-    chunks continue from it).  q is packed [total_q][Hq][D]; returns
-    (out [total_q][Hq][D], lse [total_q][Hq]) float64."""
+    chunks continue from it) -- or, with a window W, to keys p - W + 1 .. p.  q is
+    packed [total_q][Hq][D]; returns (out [total_q][Hq][D], lse [total_q][Hq])
+    float64."""
     T, Hq, D = q.shape
     Hkv = pool.shape[2]
     G = Hq // Hkv
@@ -174,11 +189,15 @@ def prefill_chunk(pool, block_tables, context_lens, cu_q_lens, q, q_dtype, sm_sc
         C, L = b - a, int(context_lens[s])
         if C == 0:
             continue
-        limits = L - C + np.arange(C) + 1          # keys t < p_i + 1
+        pos = L - C + np.arange(C)
+        lo = window_start(int(pos[0]), window)     # keys before the first query's window
+        limits = pos + 1 - lo                      # keys t < p_i + 1 (gathered from lo)
+        lower = np.array([window_start(int(p), window) for p in pos]) - lo
         for g in range(Hkv):
-            K, V = gather(pool, block_tables[s], L, g, kv_dtype, k_scale, v_scale)
+            K, V = gather(pool, block_tables[s], L, g, kv_dtype, k_scale, v_scale, start=lo)
             rows = to_f64(q[a:b, g * G:(g + 1) * G], q_dtype).reshape(C * G, D)
-            o, l = attend_rows(rows, K, V, np.float32(sm_scale), np.repeat(limits, G))
+            o, l = attend_rows(rows, K, V, np.float32(sm_scale), np.repeat(limits, G),
+                               lower=np.repeat(lower, G))
             out[a:b, g * G:(g + 1) * G] = o.reshape(C, G, D)
             lse[a:b, g * G:(g + 1) * G] = l.reshape(C, G)
     return out, lse

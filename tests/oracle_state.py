@@ -42,10 +42,10 @@ def oracle_outputs(wl, pool):
     if npf:
         pf = oracle.prefill_chunk(pool, wl.block_tables[:npf], wl.context_lens[:npf],
                                   cu[:npf + 1], q[:cu[npf]], wl.q_dtype, wl.sm_scale,
-                                  wl.kv_dtype, ks, vs)
+                                  wl.kv_dtype, ks, vs, window=wl.window)
     dq = q[cu[npf]:]
     dec = oracle.decode(pool, wl.block_tables[npf:], wl.context_lens[npf:], dq, wl.q_dtype,
-                        wl.sm_scale, wl.kv_dtype, ks, vs)
+                        wl.sm_scale, wl.kv_dtype, ks, vs, window=wl.window)
     return dec[0], dec[1], pf[0], pf[1]
 
 
@@ -70,6 +70,6 @@ def oracle_sequence(wl, s):
     q = wl.q_packed()[cu[s]:cu[s + 1]]
     if s < wl.num_prefill:
         return oracle.prefill_chunk(pool, table, np.array([L]), np.array([0, C]), q, wl.q_dtype,
-                                    wl.sm_scale, wl.kv_dtype, ks, vs)
+                                    wl.sm_scale, wl.kv_dtype, ks, vs, window=wl.window)
     return oracle.decode(pool, table, np.array([L]), q, wl.q_dtype, wl.sm_scale, wl.kv_dtype,
-                         ks, vs)
+                         ks, vs, window=wl.window)

@@ -101,6 +101,7 @@ class Workload:
     block_tables: np.ndarray          # int32 [S][max_pages], -1 = unused
     num_prefill: int = 0
     num_splits: int = 0               # 0 = let the library choose
+    window: int = 0                   # limited attention window in tokens (0 = none)
     prefix_len: int = 0               # shared-prefix tokens (0 = none)
     group_of: np.ndarray | None = None   # int32 [S], prefix group per sequence
     group_owner: np.ndarray | None = None  # int32 [groups], a member of each group
@@ -323,9 +324,13 @@ def _cdiv(a, b):
 def make(cfg: int, **over) -> Workload:
     """Build workload `cfg` (1..6).  Keyword overrides shrink it for fast tests:
     num_seqs, len_range, num_prefill, prefill_chunk, prefill_cached, context_len,
-    prefix_len, group_size, num_splits, tokens."""
+    prefix_len, group_size, num_splits, tokens; `window` (any workload) limits every
+    query's attention to the W newest positions up to its own."""
     builders = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5, 6: _cfg6}
-    return builders[cfg](**over)
+    window = int(over.pop("window", 0))
+    wl = builders[cfg](**over)
+    wl.window = window
+    return wl
 
 
 def _cfg6(**o):
