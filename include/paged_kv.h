@@ -95,14 +95,22 @@ typedef struct pkv_cache {
  *   context_lens: [num_seqs] int32, tokens in the cache AFTER this step's append,
  *         1 <= context_lens[s] <= max_context_len.
  *   max_context_len: HOST value, an upper bound of context_lens used to size the
- *         grid; must satisfy max_context_len <= max_pages_per_seq * page_size. */
+ *         grid; must satisfy max_context_len <= max_pages_per_seq * page_size.
+ *   window: 0 = full attention; W > 0 = limited attention window: a query at
+ *         position p attends to keys max(0, p - W + 1) .. p only ([Deep dive] §11,
+ *         limited attention window: tokens outside a sliding window take no further
+ *         part in attention, and their blocks can be released).  Block-table entries
+ *         of pages that end at or before 32 * floor(lo / 32), lo = the first key the
+ *         call's earliest query of the sequence sees, are never read (the caller may
+ *         have released them: -1 or any value).  Ignored by kv_append and
+ *         paged_kv_debug_gather. */
 typedef struct pkv_seqs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t num_seqs;
   int32_t max_pages_per_seq;
   int32_t max_context_len;
-  int32_t reserved; /* must be 0 */
+  int32_t window; /* >= 0 */
 } pkv_seqs_t;
 
 /* kv_append -- write this step's new K/V rows into the slots the block tables name

@@ -39,7 +39,7 @@ class PkvCache(ctypes.Structure):
 class PkvSeqs(ctypes.Structure):
     _fields_ = [("block_tables", c_void_p), ("context_lens", c_void_p), ("num_seqs", c_int32),
                 ("max_pages_per_seq", c_int32), ("max_context_len", c_int32),
-                ("reserved", c_int32)]
+                ("window", c_int32)]
 
 
 class PagedKVError(RuntimeError):
@@ -112,13 +112,16 @@ def make_cache(pool: torch.Tensor, page_size: int, num_kv_heads: int, head_dim: 
                     _ptr(k_scale), _ptr(v_scale), _ptr(k_inv_scale), _ptr(v_inv_scale))
 
 
-def make_seqs(block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int) -> PkvSeqs:
-    """Describe int32 block tables [S][max_pages] and context lengths [S]."""
+def make_seqs(block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+              window: int = 0) -> PkvSeqs:
+    """Describe int32 block tables [S][max_pages] and context lengths [S]; window = the
+    limited attention window in tokens (0 = full attention)."""
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     assert block_tables.is_contiguous() and context_lens.is_contiguous()
     S = context_lens.shape[0]
     return PkvSeqs(_ptr(block_tables), _ptr(context_lens), S,
-                   block_tables.shape[1] if block_tables.dim() == 2 else 0, int(max_context_len), 0)
+                   block_tables.shape[1] if block_tables.dim() == 2 else 0, int(max_context_len),
+                   int(window))
 
 
 def kv_append(cache: PkvCache, seqs: PkvSeqs, k_new, v_new, cu_new_lens, total_new: int,

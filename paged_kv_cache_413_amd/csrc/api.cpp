@@ -115,8 +115,9 @@ int check_cache(const pkv_cache_t* c, pkv::CacheArgs& out) {
 
 int check_seqs(const pkv_seqs_t* s, const pkv::CacheArgs& c, pkv::SeqArgs& out) {
   if (!s) return fail(PKV_EINVAL, "seqs is NULL");
-  if (s->reserved != 0) return fail(PKV_EINVAL, "seqs->reserved must be 0");
+  if (s->window < 0) return fail(PKV_EINVAL, "seqs->window must be >= 0");
   if (s->num_seqs < 0) return fail(PKV_EINVAL, "seqs->num_seqs must be >= 0");
+  out.window = s->window;
   out.num_seqs = s->num_seqs;
   out.block_tables = s->block_tables;
   out.context_lens = s->context_lens;
@@ -264,7 +265,9 @@ PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num
   const int64_t resident = std::max(1, resident_items);
   int64_t splits = std::max<int64_t>(1, resident / std::max<int64_t>(base, 1));
   splits = std::min<int64_t>(splits, 16);
-  splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(s.max_context_len, 32) / 8));
+  const int64_t span = s.window > 0 ? std::min<int64_t>(s.max_context_len, int64_t(s.window) + max_q_len)
+                                    : s.max_context_len;  // keys one query group sees at most
+  splits = std::min<int64_t>(splits, std::max<int64_t>(1, cdiv(span, 32) / 8));
   p.splits = int(splits);
   if (p.splits == 1) return p;
   const size_t recs = size_t(total_q) * c.num_kv_heads * p.splits;

@@ -38,35 +38,42 @@
 namespace pkv {
 namespace {
 
-// Fold one block into the state of the tile's rows.  t_end: first token past this
-// range; lim_row: this lane's row sees keys t < lim_row (its causal limit: the sequence
-// length for decode); lim_min = min(t_end, smallest lim_row), wave-uniform.  On the
-// blocks that reach it the excess keys' scores are masked, and on the range's last,
-// partial block the V entries past t_end are zeroed.
+// Keys a tile row sees: lo_row <= t < lim_row (its window start and causal limit; for
+// decode 0 or the window start, and the sequence length), further cut to the range's
+// t_end.  lim_min = min(t_end, smallest lim_row) and lo_max = largest lo_row are
+// wave-uniform.
+struct RowKeys {
+  int t_end, lim_row, lim_min, lo_row, lo_max;
+};
+
+// Fold one block into the state of the tile's rows.  On the blocks that reach a row's
+// limit or start before a row's window the excluded keys' scores are masked, and on the
+// range's last, partial block the V entries past t_end are zeroed.
 template <int D>
 __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16x8 (&qf)[D / 32],
-                                           float qk_scale, int t, int t_end, int lim_row, int lim_min,
-                                           int lane) {
+                                           float qk_scale, int t, const RowKeys& k, int lane) {
   float sc[8];
   block_scores<D>(b, qf, sc);
-  if (t + BT > lim_min) {  // wave-uniform
-    const int c = lane >> 4, lim = min(t_end, lim_row);
+  if (t + BT > k.lim_min || t < k.lo_max) {  // wave-uniform
+    const int c = lane >> 4, lim = min(k.t_end, k.lim_row);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (t + tok_of(c, e) >= lim) sc[e] = -INFINITY;
-    if (t + BT > t_end) mask_v_tail<D>(b, t_end - t, lane);
+    for (int e = 0; e < 8; ++e) {
+      const int tk = t + tok_of(c, e);
+      if (tk >= lim || tk < k.lo_row) sc[e] = -INFINITY;
+    }
+    if (t + BT > k.t_end) mask_v_tail<D>(b, k.t_end - t, lane);
   }
   softmax_pv<D>(st, b, sc, qk_scale, lane);
 }
 
-// Blocks [b0, b1) of one (sequence, kv head), t_end = last token + 1 of the range.
+// Blocks [b0, b1) of one (sequence, kv head).
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
-                                          int b0, int b1, int t_end, int lim_row, int lim_min, int L, int log2P,
+                                          int b0, int b1, const RowKeys& k, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
   run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](Block<D>& b, int t) {
-    fold_block<D>(st, b, qf, qk_scale, t, t_end, lim_row, lim_min, lane);
+    fold_block<D>(st, b, qf, qk_scale, t, k, lane);
   });
 }
 
@@ -143,6 +150,9 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   if (t0 >= L) return;
   const int t1 = min(L, t0 + a.chunk);
   const int nsplit = (L + a.chunk - 1) / a.chunk;
+  // a partition wholly before the window keeps an empty state: it records lse = -inf
+  // and zeros, which the merge skips
+  const int lo = window_lo(L - 1, a.seqs.window), ts = max(t0, lo);
   float qk_scale, vscale;
   scales<KV>(a, g, qk_scale, vscale);
   bf16x8 qf[D / 32];
@@ -152,9 +162,10 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
   const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
-  run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt,
-                           t0 >> LOG2_BT, (t1 + BT - 1) >> LOG2_BT, t1, L, t1, L, a.cache.log2_page,
-                           Hkv * tile_b, g * tile_b, lane);
+  if (ts < t1)
+    run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, ts >> LOG2_BT,
+                             (t1 + BT - 1) >> LOG2_BT, RowKeys{t1, L, t1, lo, lo}, L, a.cache.log2_page,
+                             Hkv * tile_b, g * tile_b, lane);
   finish<D, G, G>(st, a, s, 1, g, nsplit == 1, int64_t(sg) * a.max_splits + split, qk_scale, vscale, lane);
 }
 
@@ -171,23 +182,38 @@ __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
   return v;
 }
 
+// Blocks of each (sequence, kv head) segment of sequence s: the 32-token blocks from
+// the one holding the first key its earliest query sees to the one holding its last
+// key (L tokens, nq queries at positions L - nq .. L - 1, window W); blo = the first.
+__device__ __forceinline__ int seg_blocks(int L, int nq, int W, int& blo) {
+  blo = window_lo(L - nq, W) >> LOG2_BT;
+  return ((L + BT - 1) >> LOG2_BT) - blo;
+}
+
+// Queries of sequence s in this call: packed rows cu[s] .. cu[s+1]-1, or the one row s.
+__device__ __forceinline__ int queries_of(const int32_t* __restrict__ cu, int s) {
+  return cu ? cu[s + 1] - cu[s] : 1;
+}
+
 // Total blocks of all (sequence, kv head) segments.
-__device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens, int S, int Hkv,
-                                                int lane) {
+__device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens, const int32_t* __restrict__ cu,
+                                                int W, int S, int Hkv, int lane) {
   int64_t sum = 0;
-  for (int s = lane; s < S; s += 64) sum += (lens[s] + BT - 1) >> LOG2_BT;
+  int blo;
+  for (int s = lane; s < S; s += 64) sum += seg_blocks(lens[s], queries_of(cu, s), W, blo);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   return uniform64(sum * Hkv);
 }
 
 // Sequence whose segments contain flat block f, and its cum (blocks before it).
-__device__ __forceinline__ void locate(const int32_t* __restrict__ lens, int S, int Hkv, int64_t f,
-                                       int lane, int& s_out, int64_t& cum_out) {
+__device__ __forceinline__ void locate(const int32_t* __restrict__ lens, const int32_t* __restrict__ cu, int W,
+                                       int S, int Hkv, int64_t f, int lane, int& s_out, int64_t& cum_out) {
   int64_t run = 0;
   for (int base = 0; base < S; base += 64) {
     const int s = base + lane;
-    const int64_t nb = s < S ? int64_t((lens[s] + BT - 1) >> LOG2_BT) : 0;
+    int blo;
+    const int64_t nb = s < S ? int64_t(seg_blocks(lens[s], queries_of(cu, s), W, blo)) : 0;
     const int64_t incl = wave_incl_scan(nb, lane);
     const uint64_t hit = __ballot(s < S && Hkv * (run + incl) > f);
     if (hit) {
@@ -214,7 +240,9 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   if (w >= a.num_waves) return;
   const int S = a.seqs.num_seqs, Hkv = a.cache.num_kv_heads;
   const int32_t* lens = a.seqs.context_lens;
-  const int64_t T = total_blocks(lens, S, Hkv, lane);
+  const int32_t* cu = MQ ? a.cu_q_lens : nullptr;
+  const int W = a.seqs.window;
+  const int64_t T = total_blocks(lens, cu, W, S, Hkv, lane);
   const int64_t share = max(int64_t(a.min_share), (T + a.num_waves - 1) / a.num_waves);
   const int64_t f0 = int64_t(w) * share;
   int4* desc = a.ws_desc + w;
@@ -225,14 +253,17 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   const int64_t fend = min(T, f0 + share);
   int s;
   int64_t cum;
-  locate(lens, S, Hkv, f0, lane, s, cum);
+  locate(lens, cu, W, S, Hkv, f0, lane, s, cum);
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
   int64_t f = f0;
   bool first = true;
   while (f < fend) {
     const int L = lens[s];
-    const int nb = (L + BT - 1) >> LOG2_BT;
+    const int q0 = MQ ? a.cu_q_lens[s] : s;
+    const int nq = MQ ? a.cu_q_lens[s + 1] - q0 : 1;
+    int blo;
+    const int nb = seg_blocks(L, nq, W, blo);
     const int64_t seg0 = Hkv * cum;
     const int g = int((f - seg0) / nb);
     const int64_t gs = seg0 + int64_t(g) * nb;            // this segment's first flat block
@@ -248,18 +279,16 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
     }
     float qk_scale, vscale;
     scales<KV>(a, g, qk_scale, vscale);
-    const int q0 = MQ ? a.cu_q_lens[s] : s;
-    const int nq = MQ ? a.cu_q_lens[s + 1] - q0 : 1;
     bf16x8 qf[D / 32];
     load_q<D, G>(qf, a.q, q0, nq, a.num_q_heads, g, lane);
     State<D> st;
     state_init(st);
     const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
-    const int t_end = min(L, b1 << LOG2_BT);
-    const int lim_row = L - nq + (lane & 15) / G + 1;  // causal limit of this lane's row
-    run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, b0, b1,
-                             t_end, lim_row, min(t_end, L - nq + 1), L, a.cache.log2_page, Hkv * tile_b,
-                             g * tile_b, lane);
+    const int t_end = min(L, (blo + b1) << LOG2_BT);
+    const int pos = L - nq + (lane & 15) / G;  // position of this lane's row's query
+    const RowKeys k{t_end, pos + 1, min(t_end, L - nq + 1), window_lo(pos, W), window_lo(L - 1, W)};
+    run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, blo + b0,
+                             blo + b1, k, L, a.cache.log2_page, Hkv * tile_b, g * tile_b, lane);
     const bool complete = b0 == 0 && b1 == nb;
     finish<D, G, ROWS>(st, a, q0, nq, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
     first = false;

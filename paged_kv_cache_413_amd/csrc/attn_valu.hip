@@ -127,6 +127,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   if (t0 >= nkeys) return;
   const int t1 = min(nkeys, t0 + a.chunk);
   const int nsplit = (nkeys + a.chunk - 1) / a.chunk;
+  // keys before the window (a partition wholly before it keeps an empty state and
+  // records lse = -inf and a zero output, which the merge skips)
+  const int tlo = max(t0, window_lo(nkeys - 1, a.seqs.window));
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane / LPR, c = lane % LPR;
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
   }
 
-  for (int tb = t0 + w * RPW; tb < t1; tb += kWaves * RPW) {
+  for (int tb = tlo + w * RPW; tb < t1; tb += kWaves * RPW) {
     const int t = tb + r;
     if (t < t1) {
       const int64_t koff = elem_offset(bt, t, a.cache.log2_page, 0, g, Hkv, D, c * 8);
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
       lsum += f * sm_l[ww][h];
       osum += f * sm_acc[ww][h][d];
     }
-    const float o = osum / lsum * vscale;
+    const float o = lsum > 0.f ? osum / lsum * vscale : 0.f;
     const float lse = (M + __log2f(lsum)) * kLn2;   // natural-log units
     const int hq = g * G + h;
     if (nsplit == 1) {
@@ -270,7 +273,8 @@ __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
   for (int j = 0; j < n; ++j) wsum += __expf(a.ws_lse[base + j] - M);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float o = 0.f;
-    for (int j = 0; j < n; ++j) o += __expf(a.ws_lse[base + j] - M) * a.ws_o[(base + j) * D + d];
+    for (int j = 0; j < n; ++j)
+      if (a.ws_lse[base + j] != -INFINITY) o += __expf(a.ws_lse[base + j] - M) * a.ws_o[(base + j) * D + d];
     store_out<QT>(a.out, (int64_t(row) * a.num_q_heads + hq) * D + d, o / wsum);
   }
   if (a.lse_out && threadIdx.x == 0) a.lse_out[int64_t(row) * a.num_q_heads + hq] = M + __logf(wsum);

@@ -31,6 +31,12 @@ __device__ __forceinline__ int64_t tile_offset(int32_t page, int kv, int head, i
 }
 
 // log2 of the V sub-block length: 32 slots, or the whole page when it is shorter.
+// First key a query at position pos attends to: 0, or under a limited attention window
+// of W tokens the oldest of the W newest positions up to its own.
+__host__ __device__ __forceinline__ int window_lo(int pos, int W) {
+  return W > 0 ? (pos - W + 1 > 0 ? pos - W + 1 : 0) : 0;
+}
+
 __host__ __device__ __forceinline__ int v_sub_log2(int log2P) { return log2P < 5 ? log2P : 5; }
 
 // Position of slot r (0..31) inside a 32-slot V sub-block: slots 4c..4c+3 go to

@@ -20,6 +20,7 @@ struct SeqArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   int num_seqs, max_pages_per_seq, max_context_len;
+  int window;  // 0 = full attention, else keys p - window + 1 .. p of a query at p
 };
 
 // kv_append

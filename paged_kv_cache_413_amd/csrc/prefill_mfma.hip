@@ -99,21 +99,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int q0 = qt * QW;
   if (q0 >= C) return;
   const int L = a.seqs.context_lens[s];
+  const int W = a.seqs.window;
   const int pos0 = L - C;                          // position of query 0 of the chunk
   const int kend = pos0 + min(C, q0 + QW);         // keys [0, kend) reach this tile
   const int nb = (kend + BT - 1) >> LOG2_BT;
-  const int b0 = int(int64_t(nb) * split / nsplit), b1 = int(int64_t(nb) * (split + 1) / nsplit);
+  const int blo = window_lo(pos0 + q0, W) >> LOG2_BT;  // blocks before the first query's window: none
+  const int b0 = blo + int(int64_t(nb - blo) * split / nsplit);
+  const int b1 = blo + int(int64_t(nb - blo) * (split + 1) / nsplit);
 
   float qk_scale, vscale;
   scales<KV>(a, g, qk_scale, vscale);
   // Q^T operands and key limits: lane (n, c) of tile r is row n = query q0 + r*QPT +
   // n/G, head g*G + n%G; it sees keys t < lim[r] (0 for rows past the chunk).
   bf16x8 qf[NT][D / 32];
-  int lim[NT];
+  int lim[NT], lo[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
     const int qi = q0 + r * QPT + n / G;
     lim[r] = qi < C ? pos0 + qi + 1 : 0;
+    lo[r] = window_lo(pos0 + qi, W);
     if (qi < C) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t(cq0 + qi) * Hq + g * G + n % G) * D + 8 * c;
 #pragma unroll
@@ -128,6 +132,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
   }
   const int lim_min = pos0 + q0 + 1;  // smallest limit of the tile's live rows
+  const int lo_max = window_lo(pos0 + min(C, q0 + QW) - 1, W);  // largest window start of its live rows
   State<D> st[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) state_init(st[r]);
@@ -144,10 +149,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
           for (int r = 0; r < NT; ++r) {
             float sc[8];
             block_scores<D>(blk, qf[r], sc);
-            if (t + BT > lim_min) {  // wave-uniform: the block reaches some row's position
+            if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (t + tok_of(c, e) >= lim[r]) sc[e] = -INFINITY;
+              for (int e = 0; e < 8; ++e) {
+                const int tk = t + tok_of(c, e);
+                if (tk >= lim[r] || tk < lo[r]) sc[e] = -INFINITY;
+              }
             }
             softmax_pv<D>(st[r], blk, sc, qk_scale, lane);
           }
@@ -234,10 +241,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   const int cq0 = a.cu_q_lens[s], C = a.cu_q_lens[s + 1] - cq0;
   if (qt * QWG >= C) return;                            // whole workgroup
   const int L = a.seqs.context_lens[s];
+  const int W = a.seqs.window;
   const int pos0 = L - C;
   const int kend = pos0 + min(C, qt * QWG + QWG);       // keys any row of the group sees
   const int nb = (kend + BT - 1) >> LOG2_BT;
-  const int b0 = int(int64_t(nb) * split / nsplit), b1 = int(int64_t(nb) * (split + 1) / nsplit);
+  const int blo = window_lo(pos0 + qt * QWG, W) >> LOG2_BT;  // blocks before the first query's window: none
+  const int b0 = blo + int(int64_t(nb - blo) * split / nsplit);
+  const int b1 = blo + int(int64_t(nb - blo) * (split + 1) / nsplit);
   const int q0 = qt * QWG + w * QWV;                    // this wave's first query
   const bool live = q0 < C;
   const int kend_w = live ? pos0 + min(C, q0 + QWV) : 0;  // keys this wave's rows see
@@ -245,11 +255,12 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   float qk_scale, vscale;
   scales<KV>(a, g, qk_scale, vscale);
   bf16x8 qf[NT][D / 32];
-  int lim[NT];
+  int lim[NT], lo[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
     const int qi = q0 + r * QPT + n / G;
     lim[r] = qi < C ? pos0 + qi + 1 : 0;
+    lo[r] = window_lo(pos0 + qi, W);
     if (qi < C) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (int64_t(cq0 + qi) * Hq + g * G + n % G) * D + 8 * c;
 #pragma unroll
@@ -264,6 +275,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     }
   }
   const int lim_min = pos0 + q0 + 1;
+  const int lo_max = live ? window_lo(pos0 + min(C, q0 + QWV) - 1, W) : 0;  // largest window start of its rows
   State<D> st[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) state_init(st[r]);
@@ -385,12 +397,14 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     const int blk2 = min(b0 + i + 2, last);
     stash(rs, (i + 2) % kPfStages, blk2);
     fetch(rs, min(b0 + i + 4, last));
-    if (t + BT > lim_min) {  // wave-uniform: the block reaches some row's position
+    if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
       for (int r = 0; r < NT; ++r)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t + tok_of(c, e) >= lim[r]) cur[r][e] = -INFINITY;
+        for (int e = 0; e < 8; ++e) {
+          const int tk = t + tok_of(c, e);
+          if (tk >= lim[r] || tk < lo[r]) cur[r][e] = -INFINITY;
+        }
     }
     float off[NT];
     softmax_head<D, NT>(st, cur, qk_scale, off, lane);

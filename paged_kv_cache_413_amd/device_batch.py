@@ -98,7 +98,7 @@ class DeviceBatch:
         if npf:
             self.bt_pf = self.block_tables[:npf]
             self.ctx_pf = self.context_lens[:npf]
-            self.seqs_pf = B.make_seqs(self.bt_pf, self.ctx_pf, int(wl.context_lens[:npf].max()))
+            self.seqs_pf = B.make_seqs(self.bt_pf, self.ctx_pf, int(wl.context_lens[:npf].max()), wl.window)
             self.cu_q = torch.from_numpy(cu_all[:npf + 1].copy()).to(dev)
             self.q_pf = self.q[:self.npf_q]
             self.out_pf = torch.empty((self.npf_q, Hq, D), dtype=qdt, device=dev)
@@ -115,7 +115,7 @@ class DeviceBatch:
         self.ctx_dec = self.context_lens[npf:]
         self.q_dec = self.q[self.npf_q:]
         dec_max = int(wl.context_lens[npf:].max()) if self.ndec else 1
-        self.seqs_dec = B.make_seqs(self.bt_dec, self.ctx_dec, dec_max)
+        self.seqs_dec = B.make_seqs(self.bt_dec, self.ctx_dec, dec_max, wl.window)
         self.out_dec = torch.empty((self.ndec, Hq, D), dtype=qdt, device=dev)
         self.lse_dec = torch.empty((self.ndec, Hq), dtype=torch.float32, device=dev)
         ws = (B.paged_attn_decode_workspace_size(self.cache, self.seqs_dec, self.q_code, Hq, self.num_splits)

@@ -42,9 +42,9 @@ def _cache(**kw):
 
 
 def _seqs(**kw):
-    d = dict(bt=0x2000, ctx=0x3000, num_seqs=2, max_pages=4, max_len=64, reserved=0)
+    d = dict(bt=0x2000, ctx=0x3000, num_seqs=2, max_pages=4, max_len=64, window=0)
     d.update(kw)
-    return B.PkvSeqs(d["bt"], d["ctx"], d["num_seqs"], d["max_pages"], d["max_len"], d["reserved"])
+    return B.PkvSeqs(d["bt"], d["ctx"], d["num_seqs"], d["max_pages"], d["max_len"], d["window"])
 
 
 def _decode(lib, cache, seqs, q=0x4000, q_dtype=B.PKV_BF16, hq=4, splits=0, out=0x5000, ws=None, wsb=0):
@@ -71,7 +71,7 @@ def test_bad_cache_rejected(lib, kw, code):
     (dict(ctx=0), B.PKV_EINVAL),
     (dict(max_len=65), B.PKV_EINVAL),             # > max_pages * page_size
     (dict(max_len=0), B.PKV_EINVAL),
-    (dict(reserved=1), B.PKV_EINVAL),
+    (dict(window=-1), B.PKV_EINVAL),
     (dict(num_seqs=-1), B.PKV_EINVAL),
 ])
 def test_bad_seqs_rejected(lib, kw, code):
