@@ -88,6 +88,8 @@ def algorithmic_bytes(wl) -> dict:
     rows = attention_rows(wl)
     L = wl.context_lens[rows].astype(np.int64)
     nq = int(wl.new_lens[rows].sum())
+    if wl.window > 0:  # keys from the earliest query's window start
+        L = L - np.maximum(0, L - wl.new_lens[rows] - wl.window + 1)
     kv = int(L.sum()) * 2 * wl.num_kv_heads * wl.head_dim * elem
     qo = 2 * nq * wl.num_q_heads * wl.head_dim * qel
     bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + len(rows) * 4
@@ -134,13 +136,13 @@ def cpu_baseline(wl, budget_s: float):
                       k_new, v_new, wl.in_dtype, wl.kv_dtype, kinv, vinv)
         if prefill_only:
             oracle.prefill_chunk(pool, table, wl.context_lens[rows], np.array([0, n]), q, wl.q_dtype,
-                                 wl.sm_scale, wl.kv_dtype, ks, vs)
+                                 wl.sm_scale, wl.kv_dtype, ks, vs, window=wl.window)
         else:
             oracle.decode(pool, table, wl.context_lens[rows], q, wl.q_dtype,
-                          wl.sm_scale, wl.kv_dtype, ks, vs)
+                          wl.sm_scale, wl.kv_dtype, ks, vs, window=wl.window)
         t_spent += time.perf_counter() - t0
         done.append(s)
-        bytes_done += L * 2 * wl.num_kv_heads * wl.head_dim * elem
+        bytes_done += (L - (max(0, L - n - wl.window + 1) if wl.window > 0 else 0)) * 2 * wl.num_kv_heads * wl.head_dim * elem
         del pool
         if t_spent >= budget_s:
             break
@@ -164,6 +166,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--window", type=int, default=0,
+                    help="limited attention window in tokens (0 = full attention)")
     ap.add_argument("--num-splits", type=int, default=None,
                     help="override the workload's partition count (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -199,7 +203,7 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     t_setup = time.perf_counter()
-    wl = workloads.make(cfg)
+    wl = workloads.make(cfg, window=args.window)
     wl.prefetch()
     db = DeviceBatch(wl, device="cuda:0", num_splits=args.num_splits)
     db.fill_history()
@@ -273,7 +277,7 @@ def main():
         "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_prefill": wl.num_prefill,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "page_size": wl.page_size, "kv_dtype": wl.kv_dtype,
-                   "context_tokens": int(wl.context_lens.sum()), "num_splits": ns,
+                   "context_tokens": int(wl.context_lens.sum()), "num_splits": ns, "window": wl.window,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
         "hbm_frac_step": round(kv_gbs / HBM_PEAK_GBS, 4),
