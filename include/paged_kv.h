@@ -60,12 +60,15 @@ typedef enum {
  *         page_size * head_dim elements per (page, K|V, kv head); index 0 of the
  *         second axis is K, 1 is V.  A page holds the K and V of page_size
  *         consecutive tokens of one sequence.  16-byte aligned.
- *           K tile: token-major [page_size][head_dim] (a token's row is contiguous)
+ *           K tile: [head_dim / 32][page_size][32]: 32-dim chunks, token-major
+ *                   inside a chunk (32 dims of one token are contiguous)
  *           V tile: [page_size / S][head_dim][S] with S = min(page_size, 32): dim-major
- *                   inside sub-blocks of S slots (a dim's S tokens are contiguous)
- *         V is stored transposed so that the probability-times-V product reads
- *         consecutive tokens of one dim, the operand layout of the matrix cores,
- *         and one 32-token block's V is one contiguous run.
+ *                   inside sub-blocks of S slots (a dim's S tokens are contiguous);
+ *                   with S = 32, slot r of a sub-block sits at position
+ *                   8 * ((r mod 16) div 4) + 4 * (r div 16) + (r mod 4)
+ *         Both are the operand layouts of the matrix cores, so that every 64-lane
+ *         load is one contiguous kilobyte; one 32-token block's V is one run.
+ *         A page, [2][num_kv_heads][tile], is one contiguous range of the pool.
  *   page_size: power of two, >= 2.     head_dim: 64 or 128.
  *   k_scale / v_scale: FP8 only, [num_kv_heads] float32 dequantization
  *         multipliers (value = decoded code * scale); NULL for F32/BF16 caches.
@@ -130,6 +133,21 @@ typedef struct pkv_seqs {
 int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_new,
               const void* v_new, const int32_t* cu_new_lens, int32_t total_new,
               void* stream);
+
+/* kv_copy_pages -- copy whole pages of the pool: page dst_pages[i] <- page
+ * src_pages[i], K and V of every kv head, for i < num_pairs.  For copy-on-partial-
+ * reuse ([Deep dive] §11, partial reuse: when a new request matches only the first
+ * tokens of a cached block, those tokens are copied into a new block of its own, so
+ * that several requests can reuse one block partly).  The destination's slots past
+ * the matched tokens hold the source's later tokens; the new sequence's kv_append
+ * overwrites them before any attention call reads them (attention reads only slots
+ * below a sequence's length).
+ *   src_pages, dst_pages: [num_pairs] int32 page ids in [0, num_pages); a destination
+ *         page must not be a source page of the same call nor appear twice.
+ *   num_pairs: HOST value, 0 .. 65535 (0 is a no-op).
+ * Pool pages must be 16-byte multiples (always true for the supported sizes). */
+int kv_copy_pages(const pkv_cache_t* cache, const int32_t* src_pages, const int32_t* dst_pages,
+                  int32_t num_pairs, void* stream);
 
 /* Workspace bytes paged_attn_decode needs for these arguments (0 when the call
  * runs as one partition per sequence).  Same argument rules as the call; 0 is also

@@ -24,6 +24,6 @@ small inputs, the pages' worked block-table example, torch's float8_e4m3fn cast)
 """
 from .fp8_e4m3 import decode_table, encode_e4m3, decode_e4m3  # noqa: F401
 from .paged_attention import (  # noqa: F401
-    new_pool, encode_rows, append, slot_of, gather, decode, prefill_chunk,
+    new_pool, encode_rows, append, copy_pages, slot_of, gather, decode, prefill_chunk,
     attend_rows, partition_stats, lse_merge,
 )

@@ -92,6 +92,14 @@ def append(pool, block_tables, context_lens, new_lens, k_new, v_new, in_dtype, k
     return written
 
 
+def copy_pages(pool, src_pages, dst_pages):
+    """Page dst[i] becomes a copy of page src[i] (all of its K and V), for every i:
+    copy-on-partial-reuse gives a request that matches only the first tokens of a
+    cached block a block of its own holding them ([Deep dive] §11, partial reuse)."""
+    for s, d in zip(src_pages, dst_pages):
+        pool[int(d)] = pool[int(s)]
+
+
 def gather(pool, block_table_row, L: int, g: int, kv_dtype: str, k_scale=None, v_scale=None,
            start: int = 0):
     """K, V of tokens start..L-1 of one sequence and kv head g, as float64 [L-start][D]."""

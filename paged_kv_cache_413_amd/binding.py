@@ -24,7 +24,7 @@ STATUS_NAMES = {-1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE", 
 TORCH_DTYPE = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: torch.uint8}
 DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
-EXPORTS = ("kv_append", "paged_attn_decode_workspace_size", "paged_attn_decode",
+EXPORTS = ("kv_append", "kv_copy_pages", "paged_attn_decode_workspace_size", "paged_attn_decode",
            "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
            "paged_kv_debug_gather", "paged_kv_last_error")
 
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH):
     P = ctypes.POINTER
     lib.kv_append.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
     lib.kv_append.restype = c_int32
+    lib.kv_copy_pages.argtypes = [P(PkvCache), c_void_p, c_void_p, c_int32, c_void_p]
+    lib.kv_copy_pages.restype = c_int32
     lib.paged_attn_decode_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32, c_int32]
     lib.paged_attn_decode_workspace_size.restype = c_size_t
     lib.paged_attn_decode.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
@@ -128,6 +130,11 @@ def kv_append(cache: PkvCache, seqs: PkvSeqs, k_new, v_new, cu_new_lens, total_n
               stream=None):
     _check(load().kv_append(ctypes.byref(cache), ctypes.byref(seqs), _ptr(k_new), _ptr(v_new),
                             _ptr(cu_new_lens), int(total_new), _stream(stream)))
+
+
+def kv_copy_pages(cache: PkvCache, src_pages, dst_pages, num_pairs: int, stream=None):
+    _check(load().kv_copy_pages(ctypes.byref(cache), _ptr(src_pages), _ptr(dst_pages), int(num_pairs),
+                                _stream(stream)))
 
 
 def paged_attn_decode_workspace_size(cache: PkvCache, seqs: PkvSeqs, q_dtype: int,

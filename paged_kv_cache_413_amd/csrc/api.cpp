@@ -315,6 +315,19 @@ int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_ne
                        "kv_append");
 }
 
+int kv_copy_pages(const pkv_cache_t* cache, const int32_t* src_pages, const int32_t* dst_pages,
+                  int32_t num_pairs, void* stream) {
+  pkv::CacheArgs c;
+  int st;
+  if ((st = check_cache(cache, c)) != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_EINVAL, "num_pairs must be >= 0");
+  if (num_pairs > 65535) return fail(PKV_EINVAL, "num_pairs must be <= 65535 per call");
+  if (num_pairs == 0) return ok();
+  if (!src_pages || !dst_pages) return fail(PKV_EINVAL, "src_pages and dst_pages must not be NULL");
+  return launch_status(pkv::launch_copy_pages(c, src_pages, dst_pages, num_pairs, static_cast<hipStream_t>(stream)),
+                       "kv_copy_pages");
+}
+
 size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
                                         int32_t q_dtype, int32_t num_q_heads, int32_t num_splits) {
   pkv::CacheArgs c;

@@ -10,6 +10,8 @@
 // (K|V, head) row, so a bf16 row of 8 heads x 128 dims is 256 threads x 16 bytes read.
 // K rows are stored with one vector store; V goes to the dim-major V tile, one
 // element per dim.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -140,7 +142,31 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs 
   }
 }
 
+// Copy whole pages: page dst[i] <- page src[i], for i < n.  A page ([2][Hkv][tile]) is
+// one contiguous range of the pool, so the copy is a plain 16-byte-vector copy;
+// blockIdx.y = pair i, blockIdx.x strides over the page's 16-byte words.
+__global__ __launch_bounds__(256) void copy_pages_kernel(uint4* __restrict__ pool, const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int64_t words) {
+  const int i = blockIdx.y;
+  const int64_t s = src[i], d = dst[i];
+  if (s == d) return;
+  const uint4* from = pool + s * words;
+  uint4* to = pool + d * words;
+  for (int64_t w = int64_t(blockIdx.x) * 256 + threadIdx.x; w < words; w += int64_t(gridDim.x) * 256) to[w] = from[w];
+}
+
 }  // namespace
+
+hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32_t* dst, int n,
+                             hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int esz = c.dtype == DT_F32 ? 4 : c.dtype == DT_BF16 ? 2 : 1;
+  const int64_t words = int64_t(2) * c.num_kv_heads * c.page_size * c.head_dim * esz / 16;
+  const int64_t per = std::min<int64_t>(64, (words + 255) / 256);  // workgroups per page
+  hipLaunchKernelGGL(copy_pages_kernel, dim3(unsigned(per), unsigned(n)), dim3(256), 0, stream,
+                     static_cast<uint4*>(c.pool), src, dst, words);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const CacheArgs& c, const SeqArgs& s, const void* k_new,
                             const void* v_new, int in_dtype, const int32_t* cu_new_lens,

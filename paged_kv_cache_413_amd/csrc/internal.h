@@ -82,6 +82,8 @@ void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size,
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t stream);
 
 // Debug gather
+hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32_t* dst, int n,
+                             hipStream_t stream);
 hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,
                                hipStream_t stream);
 

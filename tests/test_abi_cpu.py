@@ -122,3 +122,14 @@ def test_prefill_rejects_bad_args(lib):
     assert f(mq=65) == B.PKV_EINVAL
     assert f(tq=-1) == B.PKV_EINVAL
     assert f(tq=0) == B.PKV_OK
+
+
+def test_copy_pages_rejects_bad_args(lib):
+    c = _cache()
+    f = lambda src=0x7000, dst=0x7100, n=2, cache=c: lib.kv_copy_pages(ctypes.byref(cache), src, dst, n, None)
+    assert f(n=-1) == B.PKV_EINVAL
+    assert f(src=0) == B.PKV_EINVAL
+    assert f(dst=0) == B.PKV_EINVAL
+    assert f(n=65536) == B.PKV_EINVAL
+    assert f(cache=_cache(pool=0)) == B.PKV_EINVAL
+    assert f(n=0, src=0, dst=0) == B.PKV_OK          # nothing to copy: no launch
