@@ -155,6 +155,42 @@ def cpu_baseline(wl, budget_s: float):
             "seconds": round(t_spent, 3)}
 
 
+def page_copy_bench(wl, n, steps, warmup):
+    """kv_copy_pages on n (source, destination) pairs of a pool shaped as the workload's
+    (distinct pages, the second half of the pool copied onto the first): its read and
+    write bytes per second against the HBM peak."""
+    import torch
+    from paged_kv_cache_413_amd import binding
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    page_bytes = 2 * wl.num_kv_heads * wl.page_size * wl.head_dim * esz
+    npages = 2 * n
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.kv_dtype]
+    pool = torch.zeros((npages, 2, wl.num_kv_heads, wl.page_size, wl.head_dim), dtype=dt, device="cuda")
+    code = {"f32": binding.PKV_F32, "bf16": binding.PKV_BF16, "fp8": binding.PKV_FP8_E4M3}[wl.kv_dtype]
+    cache = binding.make_cache(pool, wl.page_size, wl.num_kv_heads, wl.head_dim, code)
+    src = torch.arange(n, 2 * n, dtype=torch.int32, device="cuda")
+    dst = torch.randperm(n, device="cuda").to(torch.int32)
+    for _ in range(warmup):
+        binding.kv_copy_pages(cache, src, dst, n)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        binding.kv_copy_pages(cache, src, dst, n)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    moved = 2 * n * page_bytes
+    gbs = moved / (us * 1e-6) / 1e9
+    print(json.dumps({"metric": "kv_copy_pages: bytes read + written per second", "value": round(gbs, 2),
+                      "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "us_per_call": round(us, 2),
+                      "higher_is_better": True, "dtype": wl.kv_dtype, "data": "synthetic",
+                      "config": {"workload": f"copy {n} pages of {wl.name}'s shape", "page_bytes": page_bytes},
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "algorithmic_bytes": moved}}), flush=True)
+
+
 def _fill(wl):
     import workloads
     return workloads.fill_bits(wl.kv_dtype)
@@ -172,6 +208,9 @@ def main():
                     help="override the workload's partition count (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--page-copy", type=int, default=0,
+                    help="only time kv_copy_pages on this many page pairs of the workload's pool "
+                         "(K steps back to back between two events), print its JSON line, exit")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="only run a plain device-to-device copy of this many MB, --steps times "
                          "(the known-size reference for the HBM byte counters), then exit")
@@ -202,6 +241,9 @@ def main():
     binding.load()  # raises when libpagedkv.so is missing: there is no other path
 
     cfg = WORKLOADS[args.workload]
+    if args.page_copy > 0:
+        page_copy_bench(workloads.make(cfg), args.page_copy, args.steps, args.warmup)
+        return
     t_setup = time.perf_counter()
     wl = workloads.make(cfg, window=args.window)
     wl.prefetch()
