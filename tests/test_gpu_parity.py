@@ -484,3 +484,33 @@ def test_prefix_reuse_with_partial_page_copy(gpu_lib, P):
     ref_o, ref_l = oracle.decode(opool, otab, np.array([La, Lb]), bits(q), "bf16", np.float32(1.0 / np.sqrt(D)), "bf16")
     assert_close(out.float().cpu().numpy().astype(np.float64), ref_o, "bf16", f"P={P}")
     assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_l, "bf16", f"P={P}")
+
+
+FP8_PREFILL = [
+    # (page_size, chunks, cached, num_q_heads, num_kv_heads, head_dim, window)
+    (64, [70, 200], [190, 1000], 32, 8, 128, 0),       # LDS-shared prefill kernel
+    (16, [40, 9], [31, 300], 64, 8, 128, 0),           # per-wave kernel (pages of 16), G = 8
+    (64, [4, 3, 1], [500, 64, 2000], 32, 8, 128, 0),   # short chunks: decode kernels
+    (128, [100, 33], [0, 700], 16, 8, 64, 90),         # D = 64, G = 2, window
+]
+
+
+@pytest.mark.parametrize("P,chunks,cached,hq,hkv,D,W", FP8_PREFILL)
+def test_fp8_prefill_matches_oracle(gpu_lib, P, chunks, cached, hq, hkv, D, W):
+    """Prefill-chunk attention over an FP8 (E4M3) cache with per-kv-head scales, on
+    each prefill path, decode rows in the same batch."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(3, num_seqs=4, num_prefill=len(chunks), prefill_chunk=chunks, prefill_cached=cached,
+                        median=200, clip=(1, 600), page_size=P, num_q_heads=hq, num_kv_heads=hkv,
+                        head_dim=D, kv_dtype="fp8", window=W)
+    print(f"[case] fp8 prefill P={P} chunks={chunks} Hq={hq} Hkv={hkv} D={D} W={W}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, dlse, pf, plse = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(pf, ref[2], "fp8", f"chunks={chunks}")
+    assert_lse_close(plse, ref[3], "fp8", f"chunks={chunks}")
+    assert_close(dec, ref[0], "fp8", "decode rows")
+    assert_lse_close(dlse, ref[1], "fp8", "decode rows")

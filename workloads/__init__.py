@@ -397,7 +397,7 @@ def _cfg3(**o):
     (median 1024, sigma 1.0, clipped to [16,16384]); 32/8 heads, D=128, page 64.
     Overrides for test variants: num_seqs, num_prefill, prefill_chunk and
     prefill_cached (scalars or one per prefill request), median, clip, page_size,
-    num_q_heads, num_kv_heads, head_dim, num_splits."""
+    num_q_heads, num_kv_heads, head_dim, num_splits, kv_dtype ("fp8": an E4M3 cache)."""
     S = o.get("num_seqs", 256)
     npf = o.get("num_prefill", 2)
     C = np.broadcast_to(np.asarray(o.get("prefill_chunk", 512), np.int32), (npf,))
@@ -412,9 +412,10 @@ def _cfg3(**o):
     pps = _cdiv(L, P)
     npages = _pool_for(pps)
     bt = _assign_pages(3, pps, npages)
-    return Workload("mixed_inflight_bf16", 3, o.get("num_q_heads", 32), o.get("num_kv_heads", 8),
-                    o.get("head_dim", 128), P, "bf16", "bf16", npages, L, new, bt,
-                    num_prefill=npf, num_splits=o.get("num_splits", 0))
+    kv = o.get("kv_dtype", "bf16")
+    return Workload("mixed_inflight_bf16" if kv == "bf16" else f"mixed_inflight_{kv}", 3,
+                    o.get("num_q_heads", 32), o.get("num_kv_heads", 8), o.get("head_dim", 128), P, kv,
+                    "bf16", npages, L, new, bt, num_prefill=npf, num_splits=o.get("num_splits", 0))
 
 
 def _cfg4(**o):
