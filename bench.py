@@ -46,13 +46,18 @@ KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal
 
 
 def kernel_source_hash() -> str:
+    """Hash of those sources with comments and blank space removed: an edit that only
+    touches comments leaves the compiled kernels, and so the record, as they were."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_413_amd", "csrc")
     for name in KERNEL_SOURCES:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
+            text = open(p).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            h.update(open(p, "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
