@@ -139,13 +139,13 @@ constexpr int kWgWaves = PKV_DECODE_WG_WAVES;
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t wid = int64_t(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
+  const int64_t wid = int64_t(blockIdx.x) * kWgWaves + uniform32(threadIdx.x >> 6);
   const int Hkv = a.cache.num_kv_heads;
   if (wid >= int64_t(a.seqs.num_seqs) * Hkv * a.max_splits) return;
   const int split = int(wid % a.max_splits);
   const int sg = int(wid / a.max_splits);
   const int g = sg % Hkv, s = sg / Hkv;
-  const int L = a.seqs.context_lens[s];
+  const int L = uniform32(a.seqs.context_lens[s]);
   const int t0 = split * a.chunk;
   if (t0 >= L) return;
   const int t1 = min(L, t0 + a.chunk);
@@ -236,7 +236,7 @@ template <int KV, int D, int G, bool SMALLP, bool MQ>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
   constexpr int ROWS = MQ ? 16 : G;
   const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * kWgWaves + (threadIdx.x >> 6);
+  const int w = blockIdx.x * kWgWaves + uniform32(threadIdx.x >> 6);
   if (w >= a.num_waves) return;
   const int S = a.seqs.num_seqs, Hkv = a.cache.num_kv_heads;
   const int32_t* lens = a.seqs.context_lens;
@@ -259,9 +259,9 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   int64_t f = f0;
   bool first = true;
   while (f < fend) {
-    const int L = lens[s];
-    const int q0 = MQ ? a.cu_q_lens[s] : s;
-    const int nq = MQ ? a.cu_q_lens[s + 1] - q0 : 1;
+    const int L = uniform32(lens[s]);
+    const int q0 = MQ ? uniform32(a.cu_q_lens[s]) : s;
+    const int nq = MQ ? uniform32(a.cu_q_lens[s + 1]) - q0 : 1;
     int blo;
     const int nb = seg_blocks(L, nq, W, blo);
     const int64_t seg0 = Hkv * cum;

@@ -78,6 +78,24 @@ __device__ __forceinline__ bf16x8 load8(const char* __restrict__ base, uint32_t 
   return f.v;
 }
 
+// A value every lane holds equally, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// A 32-bit value every lane holds equally (a load from a wave-uniform address), in a
+// scalar register: what is derived from it -- block ranges, loop bounds, tile
+// addresses -- stays scalar, and the block loops branch on scalar conditions.
+__device__ __forceinline__ int uniform32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A tile address every lane holds equally, in scalar registers: a buffer descriptor
+// built from it is then known to be uniform, and its loads need no per-load check.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  return reinterpret_cast<const char*>(uniform64(reinterpret_cast<int64_t>(p)));
+}
+
 // Buffer descriptor of one tile (wave-uniform, 4 scalar registers): loads address it
 // with the lane's fixed 32-bit offset plus a scalar offset, and anything past the
 // tile's `bytes` reads as zero instead of touching other memory.  Word 3 is the
@@ -170,32 +188,29 @@ __device__ __forceinline__ void load_window(PageWindow& w, const int32_t* __rest
   w.ids = base + lane < npages ? bt[base + lane] : 0;
 }
 
-// Page of logical page p, refilling the window when p has left it (at most once per
-// 64 pages).
-__device__ __forceinline__ int32_t page_of(PageWindow& w, const int32_t* __restrict__ bt, int p,
-                                           int npages, int lane) {
-  if (p - w.base >= 64) load_window(w, bt, p, npages, lane);
+// Page of logical page p, which lies in the window.
+__device__ __forceinline__ int32_t page_of(const PageWindow& w, int p) {
   return __builtin_amdgcn_readlane(w.ids, p - w.base);
 }
 
 // Issue the loads of the block starting at token t (a multiple of 32) of the sequence
 // whose table row is bt.  With pages of >= 32 tokens the block lies in one page, whose
-// id comes from the page window, and every address is that page's tile base
-// (uniform) plus the lane's fixed offset.  Shorter pages (SMALLP) take the page of
+// id comes from the page window (which must hold it), and every address is that
+// page's tile base (uniform) plus the lane's fixed offset.  Shorter pages (SMALLP) take the page of
 // each lane's own tokens from the table, and skip tokens at or past L (the sequence
 // length): their page may not exist.
 template <int KV, int D, bool SMALLP>
 __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__ pool,
-                                           const int32_t* __restrict__ bt, PageWindow& win, int t,
+                                           const int32_t* __restrict__ bt, const PageWindow& win, int t,
                                            int L, int log2P, int64_t kv_stride_b, int64_t head_off_b,
                                            LaneOffsets lo, int lane) {
   constexpr int esz = KV == DT_BF16 ? 2 : 1;
   const int P = 1 << log2P;
   if constexpr (!SMALLP) {
-    const int32_t page = page_of(win, bt, t >> log2P, (L + P - 1) >> log2P, lane);
+    const int32_t page = page_of(win, t >> log2P);
     const uint32_t slot0 = uint32_t(t & (P - 1));
     const uint32_t tile_bytes = uint32_t(P) * D * esz;
-    const char* K = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
+    const char* K = uniform_ptr(pool + int64_t(page) * 2 * kv_stride_b + head_off_b);
     const auto rk = tile_rsrc(K, tile_bytes);
     const auto rv = tile_rsrc(K + kv_stride_b, tile_bytes);
     const uint32_t ks = slot0 * 32 * esz, vs = slot0 * D * esz;  // V: sub-block slot0/32
@@ -626,18 +641,17 @@ __device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&
   }
 }
 
-// Blocks [b0, b1) of one (sequence, kv head), folded in order by fold(block, t0).
-// PKV_DECODE_DEPTH register buffers rotate: while block i is folded the loads of the
-// next DEPTH-1 blocks are in flight.  Inside the loop every prefetch is
-// unconditional, so each fold waits only for its own block's loads (a partial
-// vmcnt), never for prefetches issued after them; the last blocks are peeled.
+// Blocks [b0, b1) of one (sequence, kv head), folded in order by fold(block, t0), all
+// of whose pages lie in the window `win` (unused with SMALLP).  PKV_DECODE_DEPTH
+// register buffers rotate: while block i is folded the loads of the next DEPTH-1
+// blocks are in flight.  Inside the loop every prefetch is unconditional, so each
+// fold waits only for its own block's loads (a partial vmcnt), never for prefetches
+// issued after them; the last blocks are peeled.
 template <int KV, int D, bool SMALLP, typename FoldFn>
-__device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
-                                           int b0, int b1, int L, int log2P, int64_t kv_stride_b,
-                                           int64_t head_off_b, int lane, FoldFn fold) {
+__device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
+                                                const PageWindow& win, int b0, int b1, int L, int log2P,
+                                                int64_t kv_stride_b, int64_t head_off_b, int lane, FoldFn& fold) {
   const LaneOffsets lo = lane_offsets<KV, D>(lane);
-  PageWindow win;
-  if constexpr (!SMALLP) load_window(win, bt, (b0 << LOG2_BT) >> log2P, (L + (1 << log2P) - 1) >> log2P, lane);
   auto ld = [&](Block<D>& b, int blk) {
     load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
   };
@@ -693,12 +707,32 @@ __device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const 
   }
 }
 
-// A value every lane holds equally, moved to scalar registers.
-__device__ __forceinline__ int64_t uniform64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
+// Blocks [b0, b1) of one (sequence, kv head), folded in order.  With pages of >= 32
+// tokens the range is cut where it leaves a 64-page window: each piece loads its
+// window, then pipelines its blocks with no table load inside the loop (a conditional
+// load there would make every iteration wait for all loads in flight, prefetches
+// included).  The pipeline drains once per 64 pages.
+template <int KV, int D, bool SMALLP, typename FoldFn>
+__device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
+                                           int b0, int b1, int L, int log2P, int64_t kv_stride_b,
+                                           int64_t head_off_b, int lane, FoldFn fold) {
+  if constexpr (SMALLP) {
+    const PageWindow none{0, 0};
+    pipeline_blocks<KV, D, true>(pool, bt, none, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, fold);
+  } else {
+    const int log2bp = log2P - LOG2_BT;  // blocks per page, log2
+    const int npages = (L + (1 << log2P) - 1) >> log2P;
+    for (int c0 = b0; c0 < b1;) {
+      const int base = c0 >> log2bp;
+      const int c1 = min(b1, (base + 64) << log2bp);
+      PageWindow win;
+      load_window(win, bt, base, npages, lane);
+      pipeline_blocks<KV, D, false>(pool, bt, win, c0, c1, L, log2P, kv_stride_b, head_off_b, lane, fold);
+      c0 = c1;
+    }
+  }
 }
+
 
 }  // namespace
 }  // namespace pkv

@@ -95,10 +95,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   if (grp >= a.seqs.num_seqs * Hkv * nsplit) return;
   const int split = grp % nsplit, sg = grp / nsplit;
   const int g = sg % Hkv, s = sg / Hkv;
-  const int cq0 = a.cu_q_lens[s], C = a.cu_q_lens[s + 1] - cq0;
+  const int cq0 = uniform32(a.cu_q_lens[s]), C = uniform32(a.cu_q_lens[s + 1]) - cq0;
   const int q0 = qt * QW;
   if (q0 >= C) return;
-  const int L = a.seqs.context_lens[s];
+  const int L = uniform32(a.seqs.context_lens[s]);
   const int W = a.seqs.window;
   const int pos0 = L - C;                          // position of query 0 of the chunk
   const int kend = pos0 + min(C, q0 + QW);         // keys [0, kend) reach this tile
@@ -238,9 +238,9 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   if (grp >= a.seqs.num_seqs * Hkv * nsplit) return;  // whole workgroup
   const int split = grp % nsplit, sg = grp / nsplit;
   const int g = sg % Hkv, s = sg / Hkv;
-  const int cq0 = a.cu_q_lens[s], C = a.cu_q_lens[s + 1] - cq0;
+  const int cq0 = uniform32(a.cu_q_lens[s]), C = uniform32(a.cu_q_lens[s + 1]) - cq0;
   if (qt * QWG >= C) return;                            // whole workgroup
-  const int L = a.seqs.context_lens[s];
+  const int L = uniform32(a.seqs.context_lens[s]);
   const int W = a.seqs.window;
   const int pos0 = L - C;
   const int kend = pos0 + min(C, qt * QWG + QWG);       // keys any row of the group sees
