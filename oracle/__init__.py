@@ -16,13 +16,15 @@ the oracle is the plain definition written out in float64 over NumPy arrays:
   output   o = sum_t w_t V_t ;  lse = max z + ln sum_t exp(z_t - max z)
 
 The FP8 codec (fp8_e4m3) is written from the OCP 8-bit floating point definition of
-E4M3, not from the pages, which only name an FP8 KV cache.
+E4M3, and the 4-bit codec (mxfp4) from the OCP Microscaling (MX) definition of MXFP4,
+not from the pages, which only name FP8 and 4-bit KV caches.
 
 Every function here is pinned against facts fixed outside itself by the tests in
 tests/test_oracle_*.py (closed forms, invariants, a library attention routine on
 small inputs, the pages' worked block-table example, torch's float8_e4m3fn cast).
 """
 from .fp8_e4m3 import decode_table, encode_e4m3, decode_e4m3  # noqa: F401
+from .mxfp4 import mx_encode, mx_decode, decode_fp4, scale_value  # noqa: F401
 from .paged_attention import (  # noqa: F401
     new_pool, encode_rows, append, copy_pages, slot_of, gather, decode, prefill_chunk,
     attend_rows, partition_stats, lse_merge,

@@ -15,7 +15,9 @@ page open; this is the paged form of the contiguous cache
 sequence axis cut into pages.
 
 Storage dtypes: "f32" (float32), "bf16" (bit patterns in uint16), "fp8" (OCP E4M3
-codes in uint8, with one float32 dequantization scale per kv head for K and for V).
+codes in uint8, with one float32 dequantization scale per kv head for K and for V),
+"mxfp4" (OCP MXFP4: a row is stored as its D E2M1 codes, one per byte, then its D/32
+E8M0 block scales, so the last pool axis has D + D/32 entries).
 
 Query head h reads kv head h // G, G = Hq / Hkv (consecutive query heads share a KV
 head; the pages do not fix the grouping and this is the plainest reading).
@@ -25,13 +27,15 @@ from __future__ import annotations
 import numpy as np
 
 from .fp8_e4m3 import decode_e4m3, encode_e4m3
+from .mxfp4 import mx_decode, mx_encode
 
-STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8, "mxfp4": np.uint8}
 
 
 def new_pool(num_pages, num_kv_heads, page_size, head_dim, kv_dtype, fill=0):
     """A pool of `num_pages` pages filled with the storage value `fill`."""
-    return np.full((num_pages, 2, num_kv_heads, page_size, head_dim), fill,
+    row = head_dim + head_dim // 32 if kv_dtype == "mxfp4" else head_dim
+    return np.full((num_pages, 2, num_kv_heads, page_size, row), fill,
                    dtype=STORAGE[kv_dtype])
 
 
@@ -64,6 +68,10 @@ def encode_rows(x: np.ndarray, in_dtype: str, kv_dtype: str, inv_scale=None) -> 
         inv = np.asarray(inv_scale, np.float32).astype(np.float64)
         prod = to_f64(x, "bf16") * inv[:, None]
         return encode_e4m3(prod.astype(np.float32))
+    if kv_dtype == "mxfp4" and in_dtype == "bf16":
+        # each row's 32-element blocks along D are encoded by themselves
+        codes, scales = mx_encode(to_f64(x, "bf16"))
+        return np.concatenate([codes, scales], axis=-1)
     raise ValueError(f"cannot store {in_dtype} in a {kv_dtype} cache")
 
 
@@ -112,6 +120,9 @@ def gather(pool, block_table_row, L: int, g: int, kv_dtype: str, k_scale=None, v
     if kv_dtype == "fp8":
         return (decode_e4m3(kb) * np.float64(np.float32(k_scale[g])),
                 decode_e4m3(vb) * np.float64(np.float32(v_scale[g])))
+    if kv_dtype == "mxfp4":
+        D = pool.shape[4] * 32 // 33
+        return mx_decode(kb[:, :D], kb[:, D:]), mx_decode(vb[:, :D], vb[:, D:])
     return to_f64(kb, kv_dtype), to_f64(vb, kv_dtype)
 
 

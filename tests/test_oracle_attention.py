@@ -56,6 +56,8 @@ def logical_kv(wl, s):
             q8 = x32.to(torch.float8_e4m3fn).double()
             out.append(q8 * torch.from_numpy(sc).double()[None, :, None])
         k, v = out
+    if wl.kv_dtype == "mxfp4":   # the codec itself is pinned in test_oracle_mxfp4.py
+        k, v = (torch.from_numpy(oracle.mx_decode(*oracle.mx_encode(x.numpy()))) for x in (k, v))
     return k, v
 
 
@@ -91,6 +93,22 @@ def test_p1_paged_oracle_equals_dense_attention(cfg):
     assert got.shape == ref.shape
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("cfg,over", [
+    (2, dict(num_seqs=4, len_range=(1, 300), kv_dtype="mxfp4")),
+    (3, dict(num_seqs=5, num_prefill=2, prefill_chunk=[40, 3], prefill_cached=[70, 33], median=40,
+             clip=(1, 150), kv_dtype="mxfp4")),
+])
+def test_p1_mxfp4_pool_equals_dense_attention_over_decoded_tokens(cfg, over):
+    """An MXFP4 pool (rows of codes and scales in paged slots) attends exactly like
+    dense attention over the decoded logical tokens."""
+    wl = workloads.make(cfg, **over)
+    pool = oracle_pool(wl)
+    dec, _, pf, _ = oracle_outputs(wl, pool)
+    ref = sdpa_reference(wl)
+    got = np.concatenate([pf, dec]) if wl.num_prefill else dec
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
 def test_p1_catches_a_planted_head_mapping_error(monkeypatch):

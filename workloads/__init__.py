@@ -79,6 +79,10 @@ def fill_bits(kv_dtype: str):
         return (np.uint16(0x7FC0), to_storage(np.array([3.0e4], np.float32), "bf16")[0])
     if kv_dtype == "fp8":
         return (np.uint8(0x7F), np.uint8(0x7E))
+    if kv_dtype == "mxfp4":
+        # bytes of codes and scales alike: 0xFF makes every scale NaN (E8M0 255);
+        # 0x97 makes scales 2^24 and codes 6 / -0.5
+        return (np.uint8(0xFF), np.uint8(0x97))
     raise ValueError(kv_dtype)
 
 
@@ -142,9 +146,11 @@ class Workload:
     def kv_bytes_logical(self) -> int:
         """K and V bytes of every attended token of the decode sequences, each read
         once per sequence (shared prefix pages counted once per sequence)."""
-        elem = {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
         L = self.context_lens[self.num_prefill:].astype(np.int64)
-        return int(L.sum()) * 2 * self.num_kv_heads * self.head_dim * elem
+        n = int(L.sum()) * 2 * self.num_kv_heads * self.head_dim
+        if self.kv_dtype == "mxfp4":       # half a byte per element + a scale byte per 32
+            return n // 2 + n // 32
+        return n * {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
 
     # ---- values ---------------------------------------------------------------------
     def _private_start(self, s: int) -> int:
@@ -375,7 +381,7 @@ def _cfg2(**o):
     """Llama-3-8B-shaped decode, bf16: 64 sequences, lengths U[512,4096], 32/8 heads,
     D=128, page 64, pool 1.25x the pages needed.  Overrides for small test variants:
     num_seqs, len_range or explicit lens, page_size, num_q_heads, num_kv_heads,
-    head_dim, num_splits."""
+    head_dim, num_splits, kv_dtype ("mxfp4": an OCP MXFP4 cache)."""
     if "lens" in o:
         L = np.array(o["lens"], np.int32)
     else:
@@ -386,8 +392,9 @@ def _cfg2(**o):
     pps = _cdiv(L, P)
     npages = _pool_for(pps)
     bt = _assign_pages(2, pps, npages)
-    return Workload("llama3_8b_decode_bf16", 2, o.get("num_q_heads", 32), o.get("num_kv_heads", 8),
-                    o.get("head_dim", 128), P, "bf16", "bf16", npages, L, np.ones_like(L), bt,
+    kv = o.get("kv_dtype", "bf16")
+    return Workload(f"llama3_8b_decode_{kv}", 2, o.get("num_q_heads", 32), o.get("num_kv_heads", 8),
+                    o.get("head_dim", 128), P, kv, "bf16", npages, L, np.ones_like(L), bt,
                     num_splits=o.get("num_splits", 0))
 
 
@@ -397,7 +404,8 @@ def _cfg3(**o):
     (median 1024, sigma 1.0, clipped to [16,16384]); 32/8 heads, D=128, page 64.
     Overrides for test variants: num_seqs, num_prefill, prefill_chunk and
     prefill_cached (scalars or one per prefill request), median, clip, page_size,
-    num_q_heads, num_kv_heads, head_dim, num_splits, kv_dtype ("fp8": an E4M3 cache)."""
+    num_q_heads, num_kv_heads, head_dim, num_splits, kv_dtype ("fp8": an E4M3 cache,
+    "mxfp4": an OCP MXFP4 cache)."""
     S = o.get("num_seqs", 256)
     npf = o.get("num_prefill", 2)
     C = np.broadcast_to(np.asarray(o.get("prefill_chunk", 512), np.int32), (npf,))
