@@ -40,7 +40,20 @@ WORKLOADS = {
     "long_context_splitkv_bf16": 4,
     "fp8_shared_prefix_decode": 5,
     "spec_verify4_bf16": 6,
+    "llama3_8b_decode_mxfp4": (2, {"kv_dtype": "mxfp4"}),
 }
+
+
+def make_workload(name: str, **over):
+    import workloads
+    spec = WORKLOADS[name]
+    cfg, base = spec if isinstance(spec, tuple) else (spec, {})
+    return workloads.make(cfg, **{**base, **over})
+
+
+def kv_bytes_per_elem(kv_dtype: str) -> float:
+    """Cache bytes per K or V element (MXFP4: half a byte plus a scale byte per 32)."""
+    return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 17.0 / 32.0}[kv_dtype]
 # sources of the decode call on the matrix-core path (the traffic record is void once any changes)
 KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp")
 
@@ -88,14 +101,14 @@ def algorithmic_bytes(wl) -> dict:
     every attended token (once per sequence), the queries and outputs, the block-table
     entries the sequences use and their lengths."""
     import numpy as np
-    elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    elem = kv_bytes_per_elem(wl.kv_dtype)
     qel = 4 if wl.q_dtype == "f32" else 2
     rows = attention_rows(wl)
     L = wl.context_lens[rows].astype(np.int64)
     nq = int(wl.new_lens[rows].sum())
     if wl.window > 0:  # keys from the earliest query's window start
         L = L - np.maximum(0, L - wl.new_lens[rows] - wl.window + 1)
-    kv = int(L.sum()) * 2 * wl.num_kv_heads * wl.head_dim * elem
+    kv = int(int(L.sum()) * 2 * wl.num_kv_heads * wl.head_dim * elem)
     qo = 2 * nq * wl.num_q_heads * wl.head_dim * qel
     bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + len(rows) * 4
     return {"kv": kv, "total": kv + qo + bt}
@@ -117,7 +130,7 @@ def cpu_baseline(wl, budget_s: float):
     _, poison = _fill(wl)
     q_all = wl.q_packed()
     cu = wl.cu(wl.new_lens)
-    elem = {"f32": 4, "bf16": 2, "fp8": 1}[wl.kv_dtype]
+    elem = kv_bytes_per_elem(wl.kv_dtype)
     done, bytes_done, t_spent = [], 0, 0.0
     for s in order:
         # a compact pool holding sequence s's pages only, with its table renumbered
@@ -245,12 +258,11 @@ def main():
         return
     binding.load()  # raises when libpagedkv.so is missing: there is no other path
 
-    cfg = WORKLOADS[args.workload]
     if args.page_copy > 0:
-        page_copy_bench(workloads.make(cfg), args.page_copy, args.steps, args.warmup)
+        page_copy_bench(make_workload(args.workload), args.page_copy, args.steps, args.warmup)
         return
     t_setup = time.perf_counter()
-    wl = workloads.make(cfg, window=args.window)
+    wl = make_workload(args.workload, window=args.window)
     wl.prefetch()
     db = DeviceBatch(wl, device="cuda:0", num_splits=args.num_splits)
     db.fill_history()

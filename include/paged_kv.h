@@ -44,7 +44,8 @@ extern "C" {
 typedef enum {
   PKV_F32 = 0,       /* IEEE binary32 */
   PKV_BF16 = 1,      /* bfloat16 */
-  PKV_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("fn": bias 7, max 448, S.1111.111 = NaN) */
+  PKV_FP8_E4M3 = 2,  /* OCP FP8 E4M3 ("fn": bias 7, max 448, S.1111.111 = NaN) */
+  PKV_MXFP4 = 3      /* OCP MXFP4: E2M1 elements, one E8M0 scale per 32 (cache only) */
 } pkv_dtype_t;
 
 typedef enum {
@@ -69,7 +70,20 @@ typedef enum {
  *         Both are the operand layouts of the matrix cores, so that every 64-lane
  *         load is one contiguous kilobyte; one 32-token block's V is one run.
  *         A page, [2][num_kv_heads][tile], is one contiguous range of the pool.
- *   page_size: power of two, >= 2.     head_dim: 64 or 128.
+ *         MXFP4 tiles (paged_kv_page_bytes gives the page size in bytes) hold
+ *         page_size * head_dim / 2 bytes of E2M1 codes, two per byte (the element
+ *         listed first in the low nibble), then page_size * head_dim / 32 E8M0
+ *         scale bytes, one per 32 consecutive dims of a token row:
+ *           K codes:  one row of head_dim / 2 bytes per slot; inside a row, dims
+ *                     32j + 8c .. 32j + 8c + 7 are the 4 bytes at 4 * (c * head_dim
+ *                     / 32 + j), c = 0..3
+ *           K scales: [page_size][head_dim / 32]
+ *           V codes:  32-slot sub-blocks of 16 * head_dim bytes; in a sub-block the
+ *                     codes of dim 16u + m at positions 8c .. 8c + 7 (positions as
+ *                     in the V tile above) are the 4 bytes at 4 * ((4m + c) *
+ *                     head_dim / 16 + u)
+ *           V scales: [page_size / 32][32 positions][head_dim / 32]
+ *   page_size: power of two, >= 2 (>= 32 for MXFP4).     head_dim: 64 or 128.
  *   k_scale / v_scale: FP8 only, [num_kv_heads] float32 dequantization
  *         multipliers (value = decoded code * scale); NULL for F32/BF16 caches.
  *   k_inv_scale / v_inv_scale: FP8 only, [num_kv_heads] float32 quantization
@@ -116,12 +130,19 @@ typedef struct pkv_seqs {
   int32_t window; /* >= 0 */
 } pkv_seqs_t;
 
+/* Bytes of one page ([2][num_kv_heads][tile]) of a pool with these parameters, for
+ * sizing pools: page_size * head_dim * 2 * num_kv_heads times the element size (4,
+ * 2 or 1 bytes; 17/32 of a byte for MXFP4, scales included).  0 for parameters
+ * pkv_cache_t does not allow. */
+size_t paged_kv_page_bytes(int32_t cache_dtype, int32_t page_size, int32_t num_kv_heads,
+                           int32_t head_dim);
+
 /* kv_append -- write this step's new K/V rows into the slots the block tables name
  * ([Deep dive] §2: a decode step writes the new token's KV; §8: each prefill
  * chunk adds its KV to the cache; [Concept] 技术原理, 调度策略嵌入: the page-table
  * lookup in front of every KV read and write).
  *   k_new, v_new: packed [total_new][num_kv_heads][head_dim]; F32 for an F32
- *         cache, BF16 for BF16 and FP8 caches.
+ *         cache, BF16 for BF16, FP8 and MXFP4 caches.
  *   cu_new_lens: [num_seqs + 1] int32 prefix sums (cu[0] = 0, cu[num_seqs] =
  *         total_new); sequence s writes rows cu[s] .. cu[s+1]-1 to positions
  *         context_lens[s] - n_s .. context_lens[s] - 1, n_s = cu[s+1] - cu[s].
@@ -129,6 +150,10 @@ typedef struct pkv_seqs {
  * Position t of sequence s lands in page block_tables[s][t / page_size], slot
  * t % page_size.  F32 and BF16 rows are copied bit for bit; an FP8 cache stores
  * e4m3(f32(x * inv_scale[head])) rounded to nearest-even and saturated to +-448.
+ * An MXFP4 cache encodes every 32 consecutive dims of a row as one block (OCP MX
+ * conversion): scale 2^(floor(log2 max|x|) - 2), clamped to [2^-127, 2^127] (2^-127
+ * for a block of zeros); elements x / scale rounded to nearest-even on the E2M1
+ * grid, magnitudes above 6 clamped to 6, sign bit from x.  Inputs must be finite.
  * Two rows of one call must not name the same slot. */
 int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_new,
               const void* v_new, const int32_t* cu_new_lens, int32_t total_new,
@@ -159,12 +184,14 @@ size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs
 /* paged_attn_decode -- one generation step: each query head of sequence s attends
  * to all context_lens[s] cached tokens, the one appended this step included
  * ([Deep dive] §2: decode reads the whole KV history each step).
- *   q: [num_seqs][num_q_heads][head_dim] of q_dtype (F32 or BF16).
+ *   q: [num_seqs][num_q_heads][head_dim] of q_dtype (F32 or BF16; BF16 only with an
+ *         MXFP4 cache, whose values are decoded to bf16 exactly: code x 2^(E-127)).
  *   num_q_heads: a multiple of num_kv_heads; query head h reads kv head
  *         h / (num_q_heads / num_kv_heads).
  *   sm_scale: logit scale (1/sqrt(head_dim) in the usual model).
  *   num_splits: 0 = the library partitions the keys itself: with a BF16 or FP8
- *         cache, BF16 queries and pages of >= 8 tokens (the matrix-core kernels)
+ *         cache, BF16 queries and pages of >= 8 tokens, or an MXFP4 cache, BF16
+ *         queries and pages of >= 32 tokens (the matrix-core kernels)
  *         the 32-token blocks of all (sequence, kv head) pairs are cut into equal
  *         contiguous shares, one per wave that fits on the device at once;
  *         otherwise page-aligned partitions of at least 256 keys.  N > 0 = split
@@ -191,7 +218,8 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
  * first).  Query i of sequence s sits at position context_lens[s] - C_s + i and
  * attends to keys 0 .. that position.
  *   q: packed [total_q][num_q_heads][head_dim] of q_dtype (F32 or BF16; BF16 with a
- *         BF16 or FP8 cache and pages of >= 8 tokens runs on the matrix cores; there,
+ *         BF16 or FP8 cache and pages of >= 8 tokens, or an MXFP4 cache and pages of
+ *         >= 32 tokens, runs on the matrix cores; there,
  *         chunks of at most 16 / G queries -- several tokens verified per sequence,
  *         as in speculative decoding -- run on the balanced decode kernels, all
  *         queries of a (sequence, kv head) sharing one pass over its keys).
@@ -220,7 +248,9 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
  * checking page addressing bit for bit.  Uses the same page-address code as the
  * attention kernels.
  *   k_out, v_out: [num_seqs][max_context_len][num_kv_heads][head_dim] of
- *         cache_dtype; rows t >= context_lens[s] are left untouched. */
+ *         cache_dtype; rows t >= context_lens[s] are left untouched.  For MXFP4 a
+ *         row is head_dim / 2 bytes of codes in dim order (two per byte, the lower
+ *         dim in the low nibble) then its head_dim / 32 scale bytes. */
 int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void* k_out,
                           void* v_out, void* stream);
 

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/paged_kv.h"
+#include "device_common.h"
 #include "internal.h"
 
 namespace {
@@ -97,8 +98,11 @@ int check_cache(const pkv_cache_t* c, pkv::CacheArgs& out) {
   if (c->num_kv_heads < 1) return fail(PKV_EINVAL, "cache->num_kv_heads must be >= 1");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(PKV_EUNSUPPORTED, "cache->head_dim must be 64 or 128 (got %d)", c->head_dim);
-  if (c->cache_dtype != PKV_F32 && c->cache_dtype != PKV_BF16 && c->cache_dtype != PKV_FP8_E4M3)
+  if (c->cache_dtype != PKV_F32 && c->cache_dtype != PKV_BF16 && c->cache_dtype != PKV_FP8_E4M3 &&
+      c->cache_dtype != PKV_MXFP4)
     return fail(PKV_EINVAL, "cache->cache_dtype %d is not a pkv_dtype_t", c->cache_dtype);
+  if (c->cache_dtype == PKV_MXFP4 && c->page_size < 32)
+    return fail(PKV_EUNSUPPORTED, "an MXFP4 cache needs pages of >= 32 tokens (got %d)", c->page_size);
   out.pool = c->pool;
   out.num_pages = c->num_pages;
   out.page_size = c->page_size;
@@ -296,6 +300,20 @@ int check_attn(const pkv::CacheArgs& c, int q_dtype, int num_q_heads, bool /*dec
 extern "C" {
 
 const char* paged_kv_last_error(void) { return g_error.c_str(); }
+
+size_t paged_kv_page_bytes(int32_t cache_dtype, int32_t page_size, int32_t num_kv_heads, int32_t head_dim) {
+  pkv_cache_t c{};
+  c.pool = reinterpret_cast<void*>(uintptr_t(256));  // a placeholder: only the sizes are checked
+  c.num_pages = 1;
+  c.page_size = page_size;
+  c.num_kv_heads = num_kv_heads;
+  c.head_dim = head_dim;
+  c.cache_dtype = cache_dtype;
+  pkv::CacheArgs a;
+  if (check_cache(&c, a) != PKV_OK) return 0;
+  ok();
+  return size_t(2) * num_kv_heads * size_t(pkv::tile_bytes(cache_dtype, page_size, head_dim));
+}
 
 int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_new,
               const void* v_new, const int32_t* cu_new_lens, int32_t total_new, void* stream) {

@@ -9,7 +9,7 @@
 // One workgroup per packed row; each thread moves 8 consecutive elements of one
 // (K|V, head) row, so a bf16 row of 8 heads x 128 dims is 256 threads x 16 bytes read.
 // K rows are stored with one vector store; V goes to the dim-major V tile, one
-// element per dim.
+// element per dim.  MXFP4 caches have kernels of their own below (block encoding).
 #include <algorithm>
 
 #include "device_common.h"
@@ -105,6 +105,161 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
   }
 }
 
+// ---- MXFP4 ----------------------------------------------------------------------------
+// Encoding of one 32-element block (OCP Microscaling conversion, as the cache
+// description states it): the scale byte is max(E - 2, 0), E the bf16 exponent field
+// of the largest magnitude (floor(log2) of a normal value is E - 127; a zero or
+// subnormal maximum takes the clamp, byte 0 = 2^-127); each element's magnitude q =
+// |x| / 2^(byte - 127) -- exact: a power-of-two scaling of a bf16 value, below 8 -- is
+// rounded to nearest on the E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even
+// code, which is a count of the midpoints q passes: strictly for midpoints whose lower
+// neighbour is even (the tie stays there), inclusively for the others; above 5 the
+// count reaches 7 (6.0), which also clamps everything above 6.
+struct MxCodes {
+  uint32_t w[4];  // nibble e of w[c] = code of element 8c + e
+  uint32_t scale;
+};
+
+__device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
+  return uint32_t(q > 0.25f) + uint32_t(q >= 0.75f) + uint32_t(q > 1.25f) + uint32_t(q >= 1.75f) +
+         uint32_t(q > 2.5f) + uint32_t(q >= 3.5f) + uint32_t(q > 5.0f);
+}
+
+// 32 consecutive bf16 values at `src` (64-byte aligned).
+__device__ __forceinline__ MxCodes mx_encode32(const uint16_t* __restrict__ src) {
+  uint32_t h[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+    h[4 * i] = v.x;
+    h[4 * i + 1] = v.y;
+    h[4 * i + 2] = v.z;
+    h[4 * i + 3] = v.w;
+  }
+  uint32_t amax = 0;  // largest magnitude as bf16 bits (ordered like the values)
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(h[i] & 0x7fffu, (h[i] >> 16) & 0x7fffu));
+  const uint32_t E = amax >> 7;
+  MxCodes r;
+  r.scale = E >= 2 ? E - 2 : 0;
+  const float inv = __uint_as_float((254u - r.scale) << 23);  // 2^(127 - byte), a normal float
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * c + e;
+      const uint32_t bits = (h[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      const float q = __uint_as_float((bits & 0x7fffu) << 16) * inv;
+      w |= (e2m1_magnitude(q) | ((bits >> 12) & 8u)) << (4 * e);
+    }
+    r.w[c] = w;
+  }
+  return r;
+}
+
+// MXFP4 append: one 64-thread workgroup per packed row; a thread encodes one 32-dim
+// block of one (K|V, kv head) row.  K blocks go to the token's own row (four words and
+// a scale byte).  Two consecutive slots 2i, 2i+1 share their V code bytes (one nibble
+// each), so the V bytes of a pair are written by one thread only: the row of the
+// pair's first token that is new in this call.  It encodes every new token of the pair
+// and keeps the nibble of a token that is not (already cached, or not yet written).
+__global__ __launch_bounds__(64) void kv_append_mx_kernel(CacheArgs c, SeqArgs sq,
+                                                          const uint16_t* __restrict__ k_new,
+                                                          const uint16_t* __restrict__ v_new,
+                                                          const int32_t* __restrict__ cu) {
+  const int row = blockIdx.x;
+  const int s = owner_of(cu, sq.num_seqs, row);
+  const int first = cu[s], n = cu[s + 1] - first;
+  const int L = sq.context_lens[s], pos0 = L - n;
+  const int pos = pos0 + (row - first);
+  const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
+  const int D = c.head_dim, H = c.num_kv_heads, P = c.page_size, J = D / 32;
+  const int64_t tb = tile_bytes(DT_MXFP4, P, D);
+  uint8_t* pool = static_cast<uint8_t*>(c.pool);
+  const int32_t page = bt[pos >> c.log2_page];
+  const int slot = pos & (P - 1);
+  const bool v_owner = !(pos & 1) || pos - 1 < pos0;
+  for (int i = threadIdx.x; i < 2 * H * J; i += blockDim.x) {
+    const int kv = i >= H * J;
+    const int hj = i - kv * H * J;
+    const int h = hj / J, j = hj - (hj / J) * J;
+    uint8_t* tile = pool + ((int64_t(page) * 2 + kv) * H + h) * tb;
+    if (!kv) {
+      const MxCodes e = mx_encode32(k_new + (int64_t(row) * H + h) * D + 32 * j);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(tile + mx_k_word(slot, 32 * j + 8 * q, D)) = e.w[q];
+      tile[mx_k_scale(P, slot, j, D)] = uint8_t(e.scale);
+    } else if (v_owner) {
+      const int pb = pos & ~1, sl = slot & ~1;  // the pair's first position and slot
+      MxCodes e[2];
+      bool fresh[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = pb + u;
+        fresh[u] = p >= pos0 && p < L;
+        if (fresh[u]) {
+          e[u] = mx_encode32(v_new + (int64_t(first + p - pos0) * H + h) * D + 32 * j);
+          tile[mx_v_scale(P, sl + u, j, D)] = uint8_t(e[u].scale);
+        } else {
+          e[u] = MxCodes{{0u, 0u, 0u, 0u}, 0u};
+        }
+      }
+      const uint32_t keep = (fresh[0] ? 0u : 0x0fu) | (fresh[1] ? 0u : 0xf0u);
+      for (int d = 0; d < 32; ++d) {
+        uint8_t* byte = tile + mx_v_byte(sl, 32 * j + d, D);  // low nibble: slot sl, high: sl + 1
+        const uint32_t lo = (e[0].w[d >> 3] >> (4 * (d & 7))) & 15u;
+        const uint32_t hi = (e[1].w[d >> 3] >> (4 * (d & 7))) & 15u;
+        const uint32_t old = keep ? uint32_t(*byte) : 0u;
+        *byte = uint8_t((old & keep) | ((lo | (hi << 4)) & ~keep));
+      }
+    }
+  }
+}
+
+// MXFP4 gather: one workgroup per (4-token block, sequence); a thread writes one 32-dim
+// block of one logical (token, K|V, head) row -- its 16 code bytes in dim order and its
+// scale byte -- reading the tile through the same offset functions as the append.
+__global__ __launch_bounds__(256) void debug_gather_mx_kernel(CacheArgs c, SeqArgs sq,
+                                                              uint8_t* __restrict__ k_out,
+                                                              uint8_t* __restrict__ v_out) {
+  const int s = blockIdx.y;
+  const int L = sq.context_lens[s];
+  const int D = c.head_dim, H = c.num_kv_heads, P = c.page_size, J = D / 32;
+  const int row_bytes = D / 2 + J;
+  const int64_t tb = tile_bytes(DT_MXFP4, P, D);
+  const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
+  const uint8_t* pool = static_cast<const uint8_t*>(c.pool);
+  const int t0 = blockIdx.x * 4;
+  for (int i = threadIdx.x; i < 4 * 2 * H * J; i += blockDim.x) {
+    const int tt = i / (2 * H * J);
+    const int t = t0 + tt;
+    if (t >= L) continue;
+    const int rem = i - tt * 2 * H * J;
+    const int kv = rem >= H * J;
+    const int hj = rem - kv * H * J;
+    const int h = hj / J, j = hj - (hj / J) * J;
+    const int slot = t & (P - 1);
+    const uint8_t* tile = pool + ((int64_t(bt[t >> c.log2_page]) * 2 + kv) * H + h) * tb;
+    uint8_t* out = (kv ? v_out : k_out) + ((int64_t(s) * sq.max_context_len + t) * H + h) * row_bytes;
+    for (int b = 0; b < 16; ++b) {
+      uint32_t two = 0;
+      for (int u = 0; u < 2; ++u) {
+        const int d = 32 * j + 2 * b + u;
+        uint32_t nib;
+        if (!kv) {
+          nib = (*reinterpret_cast<const uint32_t*>(tile + mx_k_word(slot, d, D)) >> (4 * (d & 7))) & 15u;
+        } else {
+          nib = (uint32_t(tile[mx_v_byte(slot, d, D)]) >> (4 * (vpos(slot & 31) & 1))) & 15u;
+        }
+        two |= nib << (4 * u);
+      }
+      out[16 * j + b] = uint8_t(two);
+    }
+    out[D / 2 + j] = tile[kv ? mx_v_scale(P, slot, j, D) : mx_k_scale(P, slot, j, D)];
+  }
+}
+
 // Gather: one workgroup per (4-token block, sequence); each thread writes 16 bytes of
 // one logical (token, K|V, head) row, read from the row (K) or column (V) of the tile.
 __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs sq,
@@ -160,8 +315,7 @@ __global__ __launch_bounds__(256) void copy_pages_kernel(uint4* __restrict__ poo
 hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32_t* dst, int n,
                              hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const int esz = c.dtype == DT_F32 ? 4 : c.dtype == DT_BF16 ? 2 : 1;
-  const int64_t words = int64_t(2) * c.num_kv_heads * c.page_size * c.head_dim * esz / 16;
+  const int64_t words = int64_t(2) * c.num_kv_heads * tile_bytes(c.dtype, c.page_size, c.head_dim) / 16;
   const int64_t per = std::min<int64_t>(64, (words + 255) / 256);  // workgroups per page
   hipLaunchKernelGGL(copy_pages_kernel, dim3(unsigned(per), unsigned(n)), dim3(256), 0, stream,
                      static_cast<uint4*>(c.pool), src, dst, words);
@@ -179,6 +333,9 @@ hipError_t launch_kv_append(const CacheArgs& c, const SeqArgs& s, const void* k_
     hipLaunchKernelGGL((kv_append_kernel<DT_BF16, DT_BF16>), grid, block, 0, stream, c, s, k_new, v_new, cu_new_lens);
   else if (c.dtype == DT_FP8 && in_dtype == DT_BF16)
     hipLaunchKernelGGL((kv_append_kernel<DT_BF16, DT_FP8>), grid, block, 0, stream, c, s, k_new, v_new, cu_new_lens);
+  else if (c.dtype == DT_MXFP4 && in_dtype == DT_BF16)
+    hipLaunchKernelGGL(kv_append_mx_kernel, grid, dim3(64), 0, stream, c, s, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), cu_new_lens);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -188,8 +345,12 @@ hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out
                                hipStream_t stream) {
   if (s.num_seqs == 0) return hipSuccess;
   const dim3 grid((s.max_context_len + 3) / 4, s.num_seqs), block(256);
-  hipLaunchKernelGGL(debug_gather_kernel, grid, block, 0, stream, c, s,
-                     static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
+  if (c.dtype == DT_MXFP4)
+    hipLaunchKernelGGL(debug_gather_mx_kernel, grid, block, 0, stream, c, s, static_cast<uint8_t*>(k_out),
+                       static_cast<uint8_t*>(v_out));
+  else
+    hipLaunchKernelGGL(debug_gather_kernel, grid, block, 0, stream, c, s,
+                       static_cast<uint8_t*>(k_out), static_cast<uint8_t*>(v_out));
   return hipGetLastError();
 }
 

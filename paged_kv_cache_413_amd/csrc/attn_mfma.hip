@@ -48,12 +48,14 @@ struct RowKeys {
 
 // Fold one block into the state of the tile's rows.  On the blocks that reach a row's
 // limit or start before a row's window the excluded keys' scores are masked, and on the
-// range's last, partial block the V entries past t_end are zeroed.
-template <int D>
-__device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16x8 (&qf)[D / 32],
+// range's last, partial block the V entries past t_end are zeroed.  An MXFP4 block is
+// decoded first (ready); a bf16 / FP8 one is used as loaded.
+template <int D, typename Blk>
+__device__ __forceinline__ void fold_block(State<D>& st, Blk& b, const bf16x8 (&qf)[D / 32],
                                            float qk_scale, int t, const RowKeys& k, int lane) {
+  const auto& r = ready<D>(b);
   float sc[8];
-  block_scores<D>(b, qf, sc);
+  block_scores<D>(r, qf, sc);
   if (t + BT > k.lim_min || t < k.lo_max) {  // wave-uniform
     const int c = lane >> 4, lim = min(k.t_end, k.lim_row);
 #pragma unroll
@@ -63,7 +65,7 @@ __device__ __forceinline__ void fold_block(State<D>& st, Block<D>& b, const bf16
     }
     if (t + BT > k.t_end) mask_v_tail<D>(b, k.t_end - t, lane);
   }
-  softmax_pv<D>(st, b, sc, qk_scale, lane);
+  softmax_pv<D>(st, r, sc, qk_scale, lane);
 }
 
 // Blocks [b0, b1) of one (sequence, kv head).
@@ -72,7 +74,7 @@ __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 3
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                           int b0, int b1, const RowKeys& k, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](Block<D>& b, int t) {
+  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](auto& b, int t) {
     fold_block<D>(st, b, qf, qk_scale, t, k, lane);
   });
 }
@@ -159,8 +161,7 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   load_q<D, G>(qf, a.q, s, 1, a.num_q_heads, g, lane);
   State<D> st;
   state_init(st);
-  constexpr int esz = KV == DT_BF16 ? 2 : 1;
-  const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
+  const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
   const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
   if (ts < t1)
     run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, ts >> LOG2_BT,
@@ -254,8 +255,7 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(P
   int s;
   int64_t cum;
   locate(lens, cu, W, S, Hkv, f0, lane, s, cum);
-  constexpr int esz = KV == DT_BF16 ? 2 : 1;
-  const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
+  const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
   int64_t f = f0;
   bool first = true;
   while (f < fend) {
@@ -371,7 +371,11 @@ hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
 
 template <int KV, int D, int G>
 hipError_t dispatch_p(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
-  return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, p, st) : launch_t<KV, D, G, true>(a, p, st);
+  if constexpr (KV == DT_MXFP4) {  // MXFP4 tiles need pages of >= 32 tokens
+    return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, p, st) : hipErrorInvalidValue;
+  } else {
+    return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, p, st) : launch_t<KV, D, G, true>(a, p, st);
+  }
 }
 
 template <int KV, int D>
@@ -395,7 +399,8 @@ hipError_t dispatch_d(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
 // representative: G only changes which MFMA rows are used).
 template <int KV, int D>
 const void* auto_kernel_for(int G, bool smallp) {
-#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, true, false>) \
+  // (MXFP4 has no short-page kernels: its instance stands in for both)
+#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, KV != DT_MXFP4, false>) \
                           : reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, false, false>))
   switch (G) {
     case 1: return PKV_K(1);
@@ -410,9 +415,10 @@ const void* auto_kernel_for(int G, bool smallp) {
 }  // namespace
 
 bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, int page_size) {
-  return (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && q_dtype == DT_BF16 &&
+  return (kv_dtype == DT_BF16 || kv_dtype == DT_FP8 || kv_dtype == DT_MXFP4) && q_dtype == DT_BF16 &&
          (head_dim == 64 || head_dim == 128) &&
-         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16) && page_size >= 8;
+         (group == 1 || group == 2 || group == 4 || group == 8 || group == 16) &&
+         page_size >= (kv_dtype == DT_MXFP4 ? BT : 8);
 }
 
 int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
@@ -420,14 +426,22 @@ int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
   const void* k = kv_dtype == DT_BF16
                       ? (head_dim == 64 ? auto_kernel_for<DT_BF16, 64>(group, smallp)
                                         : auto_kernel_for<DT_BF16, 128>(group, smallp))
-                      : (head_dim == 64 ? auto_kernel_for<DT_FP8, 64>(group, smallp)
-                                        : auto_kernel_for<DT_FP8, 128>(group, smallp));
+                  : kv_dtype == DT_FP8
+                      ? (head_dim == 64 ? auto_kernel_for<DT_FP8, 64>(group, smallp)
+                                        : auto_kernel_for<DT_FP8, 128>(group, smallp))
+                      : (head_dim == 64 ? auto_kernel_for<DT_MXFP4, 64>(group, false)
+                                        : auto_kernel_for<DT_MXFP4, 128>(group, false));
   return resident_blocks(k, 64 * kWgWaves) * kWgWaves;
 }
 
 hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
   if (a.seqs.num_seqs == 0) return hipSuccess;
-  return a.cache.dtype == DT_BF16 ? dispatch_d<DT_BF16>(a, p, st) : dispatch_d<DT_FP8>(a, p, st);
+  switch (a.cache.dtype) {
+    case DT_BF16: return dispatch_d<DT_BF16>(a, p, st);
+    case DT_FP8: return dispatch_d<DT_FP8>(a, p, st);
+    case DT_MXFP4: return dispatch_d<DT_MXFP4>(a, p, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

@@ -19,7 +19,7 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -60,6 +60,35 @@ __device__ __forceinline__ int64_t elem_offset(const int32_t* __restrict__ bt, i
 }
 
 __device__ __forceinline__ int dtype_bytes(int dt) { return dt == DT_F32 ? 4 : (dt == DT_BF16 ? 2 : 1); }
+
+// Bytes of one (page, K|V, kv head) tile.  MXFP4: P*D/2 code bytes, then P*D/32 scales.
+__host__ __device__ __forceinline__ int64_t tile_bytes(int dt, int P, int D) {
+  const int64_t n = int64_t(P) * D;
+  return dt == DT_F32 ? 4 * n : dt == DT_BF16 ? 2 * n : dt == DT_FP8 ? n : n / 2 + n / 32;
+}
+
+// ---- OCP MXFP4 tiles -------------------------------------------------------------------
+// Offsets inside an MXFP4 tile of P slots x D dims (see the cache description in
+// paged_kv.h).  K: slot t's row of D/2 code bytes holds dims 32j + 8c + e (e = 0..7) in
+// the 4-byte word c*(D/32) + j, nibble e; K scales [P][D/32] follow the codes.  V:
+// 32-slot sub-blocks of 16*D code bytes; dim 16u + m of the slot at position
+// k = 8c + e = vpos(slot % 32) is nibble e of word (4m + c)*(D/16) + u; V scales
+// [P/32][32 positions][D/32] follow the codes.  These are the lane layouts of the
+// matrix-core operands: a lane's K codes for one token are one 16-byte run (D = 128),
+// and its V codes for all dims it holds are one 32-byte run.
+__host__ __device__ __forceinline__ int64_t mx_k_word(int slot, int d, int D) {
+  return int64_t(slot) * (D / 2) + ((((d >> 3) & 3) * (D / 32) + (d >> 5)) << 2);
+}
+__host__ __device__ __forceinline__ int64_t mx_v_byte(int slot, int d, int D) {
+  const int k = vpos(slot & 31), c = k >> 3, e = k & 7, m = d & 15, u = d >> 4;
+  return int64_t(slot >> 5) * (16 * D) + ((4 * m + c) * (D / 16) + u) * 4 + (e >> 1);
+}
+__host__ __device__ __forceinline__ int64_t mx_k_scale(int P, int slot, int j, int D) {
+  return int64_t(P) * (D / 2) + int64_t(slot) * (D / 32) + j;
+}
+__host__ __device__ __forceinline__ int64_t mx_v_scale(int P, int slot, int j, int D) {
+  return int64_t(P) * (D / 2) + (int64_t(slot >> 5) * 32 + vpos(slot & 31)) * (D / 32) + j;
+}
 
 // ---- bfloat16 ------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

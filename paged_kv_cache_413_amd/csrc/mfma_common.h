@@ -14,6 +14,8 @@
 // -- and the V sub-block of the pool stores its slots in that same order.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -271,6 +273,121 @@ __device__ __forceinline__ void load_block(Block<D>& b, const char* __restrict__
   }
 }
 
+// ---- MXFP4 blocks -------------------------------------------------------------------------
+// One 32-token block of an MXFP4 tile in the lane layout of the two products (pages of
+// >= 32 tokens), as loaded: E2M1 codes, eight per word, and E8M0 scale bytes.  Lane
+// (m, c) holds K dims 32j + 8c .. +7 of tokens m and 16 + m (word j of ka, kb) with
+// their scales (byte j of ksa, ksb), the V codes of dims 16u + m at positions 8c .. 8c+7
+// (word u of v), and the V scales of those eight positions (position e, block j: byte
+// e*(D/32) + j of vs).
+template <int D>
+struct MxBlock {
+  uint32_t ka[D / 32], kb[D / 32];
+  uint32_t ksa, ksb;
+  uint32_t v[D / 16];
+  uint32_t vs[D / 16];
+};
+
+template <int KV, int D>
+using BlockOf = std::conditional_t<KV == DT_MXFP4, MxBlock<D>, Block<D>>;
+
+// `n` bytes (4, 8, 16 or 32) at voff + soff of a tile, as words.
+template <int N>
+__device__ __forceinline__ void bload_words(uint32_t* w, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (N == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, PKV_KV_LOAD_AUX);
+  } else if constexpr (N == 4) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, PKV_KV_LOAD_AUX);
+  } else if constexpr (N == 8) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PKV_KV_LOAD_AUX));
+    w[0] = v[0];
+    w[1] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < N / 16; ++h) {
+      const u32x4 v =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * h, soff, PKV_KV_LOAD_AUX));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[4 * h + i] = v[i];
+    }
+  }
+}
+
+// Issue the loads of the MXFP4 block starting at token t (a multiple of 32) of a
+// sequence; its page id comes from the window (which must hold it).  Eight loads:
+// K codes of tokens m and 16 + m (D/8 bytes each), their scales (D/32 bytes each), the
+// lane's V codes and V scales (D/4 bytes each).
+template <int D>
+__device__ __forceinline__ void load_block_mx(MxBlock<D>& b, const char* __restrict__ pool, const PageWindow& win,
+                                              int t, int log2P, int64_t kv_stride_b, int64_t head_off_b,
+                                              int lane) {
+  const int P = 1 << log2P;
+  const int32_t page = page_of(win, t >> log2P);
+  const uint32_t slot0 = uint32_t(t & (P - 1));
+  const uint32_t tb = uint32_t(tile_bytes(DT_MXFP4, P, D));
+  const char* K = uniform_ptr(pool + int64_t(page) * 2 * kv_stride_b + head_off_b);
+  const auto rk = tile_rsrc(K, tb);
+  const auto rv = tile_rsrc(K + kv_stride_b, tb);
+  const uint32_t m = lane & 15, c = lane >> 4;
+  const uint32_t codes = uint32_t(P) * (D / 2);  // scales follow the codes
+  const uint32_t kso = __builtin_amdgcn_readfirstlane(slot0 * (D / 2));
+  bload_words<D / 8>(b.ka, rk, m * (D / 2) + c * (D / 8), kso);
+  bload_words<D / 8>(b.kb, rk, (16 + m) * (D / 2) + c * (D / 8), kso);
+  const uint32_t sso = __builtin_amdgcn_readfirstlane(codes + slot0 * (D / 32));
+  bload_words<D / 32>(&b.ksa, rk, m * (D / 32), sso);
+  bload_words<D / 32>(&b.ksb, rk, (16 + m) * (D / 32), sso);
+  const uint32_t sb = slot0 >> 5;
+  bload_words<D / 4>(b.v, rv, (4 * m + c) * (D / 4), __builtin_amdgcn_readfirstlane(sb * 16 * D));
+  bload_words<D / 4>(b.vs, rv, c * (D / 4), __builtin_amdgcn_readfirstlane(codes + sb * D));
+}
+
+// E8M0 scale byte -> its value 2^(e - 127) (2^-127 is a float subnormal; 255, which the
+// encoder never writes, gives infinity).
+__device__ __forceinline__ float e8m0_value(uint32_t e) { return __builtin_ldexpf(1.0f, int(e) - 127); }
+
+// Eight E2M1 codes (nibble i = element i) times `scale`, as bf16; exact, since an E2M1
+// value times a power of two is a bf16 value (subnormal ones included).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  Frag8 f;
+  f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return f.v;
+}
+
+// An MXFP4 block decoded for the products: K exactly (code x block scale, bf16), V
+// codes unscaled (their scales differ along the tokens of a lane, the contraction
+// index, so they are applied to the softmax weights instead: O += (P * X_j) . V_j for
+// each 32-dim block j), and the V scale bytes.
+template <int D>
+struct MxReady {
+  bf16x8 ka[D / 32], kb[D / 32];
+  bf16x8 v[D / 16];
+  uint32_t vs[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ const Block<D>& ready(const Block<D>& b) { return b; }
+
+template <int D>
+__device__ __forceinline__ MxReady<D> ready(const MxBlock<D>& b) {
+  MxReady<D> r;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    r.ka[j] = fp4x8_to_bf16(b.ka[j], e8m0_value((b.ksa >> (8 * j)) & 255u));
+    r.kb[j] = fp4x8_to_bf16(b.kb[j], e8m0_value((b.ksb >> (8 * j)) & 255u));
+  }
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    r.v[u] = fp4x8_to_bf16(b.v[u], 1.0f);
+    r.vs[u] = b.vs[u];
+  }
+  return r;
+}
+
 // Online-softmax state of one wave: running max m of the raw scores q.k (per row
 // lane), the lane's share of the running sum of exp2((z - m) * scale) and the output
 // accumulator O [16 rows x D] (lane (n, c) holds rows 4c..4c+3 of dim 16*dt + n in
@@ -434,8 +551,8 @@ __device__ __forceinline__ void scales(const AttnArgs& a, int g, float& qk_scale
 
 // Raw scores^T q.k of one block for one tile of 16 query rows: lane (n, c) gets row
 // n's scores of block tokens tok_of(c, e), e = 0..7.
-template <int D>
-__device__ __forceinline__ void block_scores(const Block<D>& b, const bf16x8 (&qf)[D / 32], float (&sc)[8]) {
+template <int D, typename Blk>
+__device__ __forceinline__ void block_scores(const Blk& b, const bf16x8 (&qf)[D / 32], float (&sc)[8]) {
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
@@ -468,6 +585,11 @@ __device__ __forceinline__ void mask_v_tail(Block<D>& b, int nvalid, int lane) {
   }
 }
 
+// MXFP4 blocks need no V masking: codes are always finite, and the weight of a masked
+// key is exactly 0, which its scale (ldexp) keeps at 0 whatever the scale byte holds.
+template <int D>
+__device__ __forceinline__ void mask_v_tail(MxBlock<D>&, int, int) {}
+
 // Maximum of x over the four lanes of a score row (lanes n, n+16, n+32, n+48), in all
 // four: two lane swaps across 32 and 16 lanes (no LDS permute, no lane arithmetic).
 // The swaps' results are copied out of their vector before the bit casts: a bit cast
@@ -493,8 +615,44 @@ __device__ __forceinline__ float row_max4(float x) {
 // rare blocks that move some row's reference.
 constexpr float kRescaleLog2 = 8.f;
 
+// O += P . V for one block: P (the weights p of the lane's 8 keys, fp32) packed to bf16.
 template <int D>
-__device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, const float (&sc)[8],
+__device__ __forceinline__ void pv_product(f32x4 (&o)[D / 16], const float (&p)[8], const Block<D>& b) {
+  Frag8 pa;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    pa.w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) o[dt] = mma(pa.v, b.v[dt], o[dt]);
+}
+
+// MXFP4: for each 32-dim block j the weights carry the V scales of their keys,
+// p * 2^(E - 127) (ldexp: exact, and 0 stays 0), then multiply the unscaled codes of
+// the block's two 16-dim tiles.
+template <int D>
+__device__ __forceinline__ void pv_product(f32x4 (&o)[D / 16], const float (&p)[8], const MxReady<D>& b) {
+  constexpr int J = D / 32;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    Frag8 pa;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float x[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = 2 * w + h, byte = e * J + j;
+        const int ex = int((b.vs[byte >> 2] >> (8 * (byte & 3))) & 255u) - 127;
+        x[h] = __builtin_ldexpf(p[e], ex);
+      }
+      pa.w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[0], x[1]}, bf16x2));
+    }
+    o[2 * j] = mma(pa.v, b.v[2 * j], o[2 * j]);
+    o[2 * j + 1] = mma(pa.v, b.v[2 * j + 1], o[2 * j + 1]);
+  }
+}
+
+template <int D, typename Blk>
+__device__ __forceinline__ void softmax_pv(State<D>& st, const Blk& b, const float (&sc)[8],
                                            float scale, int lane) {
   const int c = lane >> 4;
   float bm = sc[0];
@@ -523,12 +681,7 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Block<D>& b, cons
     st.m = mref;
   }
   st.l += ps;
-  Frag8 pa;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    pa.w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) st.o[dt] = mma(pa.v, b.v[dt], st.o[dt]);
+  pv_product<D>(st.o, p, b);
 }
 
 // The same update split in two for NT tiles of 16 rows that share one block, so that
@@ -652,10 +805,13 @@ __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, c
                                                 const PageWindow& win, int b0, int b1, int L, int log2P,
                                                 int64_t kv_stride_b, int64_t head_off_b, int lane, FoldFn& fold) {
   const LaneOffsets lo = lane_offsets<KV, D>(lane);
-  auto ld = [&](Block<D>& b, int blk) {
-    load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
+  auto ld = [&](BlockOf<KV, D>& b, int blk) {
+    if constexpr (KV == DT_MXFP4)
+      load_block_mx<D>(b, pool, win, blk << LOG2_BT, log2P, kv_stride_b, head_off_b, lane);
+    else
+      load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
   };
-  Block<D> x, y;
+  BlockOf<KV, D> x, y;
   ld(x, b0);
   int blk = b0;
   if constexpr (PKV_DECODE_DEPTH == 2) {
@@ -673,7 +829,7 @@ __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, c
       fold(x, blk << LOG2_BT);
     }
   } else {
-    Block<D> z;
+    BlockOf<KV, D> z;
     if (b1 - b0 == 1) {
       fold(x, blk << LOG2_BT);
       return;

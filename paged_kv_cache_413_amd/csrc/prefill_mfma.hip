@@ -138,17 +138,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   for (int r = 0; r < NT; ++r) state_init(st[r]);
 
   if (b0 < b1) {
-    constexpr int esz = KV == DT_BF16 ? 2 : 1;
-    const int64_t tile_b = int64_t(a.cache.page_size) * D * esz;
+    const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
     const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
     run_blocks<KV, D, SMALLP>(
         static_cast<const char*>(a.cache.pool), bt, b0, b1, L, a.cache.log2_page, Hkv * tile_b,
-        g * tile_b, lane, [&](Block<D>& blk, int t) {
+        g * tile_b, lane, [&](auto& blk, int t) {
           if (t + BT > L) mask_v_tail<D>(blk, L - t, lane);
+          const auto& rb = ready<D>(blk);  // an MXFP4 block decoded once for all tiles
 #pragma unroll
           for (int r = 0; r < NT; ++r) {
             float sc[8];
-            block_scores<D>(blk, qf[r], sc);
+            block_scores<D>(rb, qf[r], sc);
             if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 if (tk >= lim[r] || tk < lo[r]) sc[e] = -INFINITY;
               }
             }
-            softmax_pv<D>(st[r], blk, sc, qk_scale, lane);
+            softmax_pv<D>(st[r], rb, sc, qk_scale, lane);
           }
         });
   }
@@ -250,7 +250,6 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   const int b1 = blo + int(int64_t(nb - blo) * (split + 1) / nsplit);
   const int q0 = qt * QWG + w * QWV;                    // this wave's first query
   const bool live = q0 < C;
-  const int kend_w = live ? pos0 + min(C, q0 + QWV) : 0;  // keys this wave's rows see
 
   float qk_scale, vscale;
   scales<KV>(a, g, qk_scale, vscale);
@@ -494,8 +493,8 @@ template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int groups = a.seqs.num_seqs * a.cache.num_kv_heads * a.max_splits;
   const int64_t grid = int64_t((groups + kXcds - 1) / kXcds) * kXcds * a.pf_qtiles;
-  if constexpr (SMALLP) {
-    hipLaunchKernelGGL((prefill_kernel<KV, D, G, true>), dim3(unsigned(grid)), dim3(64), 0, st, a);
+  if constexpr (SMALLP || KV == DT_MXFP4) {  // one wave per item (MXFP4: pages of >= 32 tokens)
+    hipLaunchKernelGGL((prefill_kernel<KV, D, G, SMALLP>), dim3(unsigned(grid)), dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((prefill_lds_kernel<KV, D, G>), dim3(unsigned(grid)), dim3(64 * kPfWaves), 0, st, a);
   }
@@ -509,7 +508,11 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 
 template <int KV, int D, int G>
 hipError_t dispatch_p(const AttnArgs& a, hipStream_t st) {
-  return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, st) : launch_t<KV, D, G, true>(a, st);
+  if constexpr (KV == DT_MXFP4) {
+    return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, st) : hipErrorInvalidValue;
+  } else {
+    return a.cache.page_size >= BT ? launch_t<KV, D, G, false>(a, st) : launch_t<KV, D, G, true>(a, st);
+  }
 }
 
 template <int KV, int D>
@@ -533,10 +536,13 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 
 void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
                            int* resident_items) {
-  const bool lds = page_size >= BT;
+  const bool lds = page_size >= BT && kv_dtype != DT_MXFP4;
   *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : kPrefillTiles);
   const void* k;
-  if (lds) {
+  if (kv_dtype == DT_MXFP4) {
+    k = head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 64, 4, false>)
+                       : reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 128, 4, false>);
+  } else if (lds) {
     k = kv_dtype == DT_BF16
             ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 64, 4>)
                               : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 128, 4>))
@@ -554,7 +560,12 @@ void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size,
 
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t st) {
   if (a.seqs.num_seqs == 0 || a.total_q == 0) return hipSuccess;
-  return a.cache.dtype == DT_BF16 ? dispatch_d<DT_BF16>(a, st) : dispatch_d<DT_FP8>(a, st);
+  switch (a.cache.dtype) {
+    case DT_BF16: return dispatch_d<DT_BF16>(a, st);
+    case DT_FP8: return dispatch_d<DT_FP8>(a, st);
+    case DT_MXFP4: return dispatch_d<DT_MXFP4>(a, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv

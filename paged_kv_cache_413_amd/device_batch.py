@@ -19,9 +19,9 @@ import torch
 import workloads
 from . import binding as B
 
-KV_CODE = {"f32": B.PKV_F32, "bf16": B.PKV_BF16, "fp8": B.PKV_FP8_E4M3}
-INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8}
-VAL_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+KV_CODE = {"f32": B.PKV_F32, "bf16": B.PKV_BF16, "fp8": B.PKV_FP8_E4M3, "mxfp4": B.PKV_MXFP4}
+INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "fp8": torch.uint8, "mxfp4": torch.uint8}
+VAL_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "mxfp4": torch.uint8}
 
 
 def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -49,7 +49,11 @@ class DeviceBatch:
         self.num_splits = wl.num_splits if num_splits is None else num_splits
         dev = self.dev
         Hkv, P, D = wl.num_kv_heads, wl.page_size, wl.head_dim
-        self.pool = torch.empty((wl.num_pages, 2, Hkv, P, D), dtype=VAL_DTYPE[wl.kv_dtype], device=dev)
+        if wl.kv_dtype == "mxfp4":  # raw tiles of codes and scales
+            tile = B.paged_kv_page_bytes(self.kv_code, P, Hkv, D) // (2 * Hkv)
+            self.pool = torch.empty((wl.num_pages, 2, Hkv, tile), dtype=torch.uint8, device=dev)
+        else:
+            self.pool = torch.empty((wl.num_pages, 2, Hkv, P, D), dtype=VAL_DTYPE[wl.kv_dtype], device=dev)
         nan, poison = workloads.fill_bits(wl.kv_dtype)
         iv = self.pool.view(INT_VIEW[wl.kv_dtype])
         iv.fill_(_bits_scalar(nan))

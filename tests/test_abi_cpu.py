@@ -133,3 +133,24 @@ def test_copy_pages_rejects_bad_args(lib):
     assert f(n=65536) == B.PKV_EINVAL
     assert f(cache=_cache(pool=0)) == B.PKV_EINVAL
     assert f(n=0, src=0, dst=0) == B.PKV_OK          # nothing to copy: no launch
+
+
+def test_page_bytes(lib):
+    f = lambda dt, P, H, D: lib.paged_kv_page_bytes(dt, P, H, D)
+    assert f(B.PKV_BF16, 64, 8, 128) == 2 * 8 * 64 * 128 * 2
+    assert f(B.PKV_FP8_E4M3, 64, 8, 128) == 2 * 8 * 64 * 128
+    assert f(B.PKV_MXFP4, 64, 8, 128) == 2 * 8 * (64 * 128 // 2 + 64 * 128 // 32)   # 17/32 byte each
+    assert f(B.PKV_MXFP4, 32, 2, 64) == 2 * 2 * (32 * 64 * 17 // 32)
+    assert f(B.PKV_MXFP4, 16, 8, 128) == 0       # MXFP4 needs pages of >= 32 tokens
+    assert f(B.PKV_BF16, 24, 8, 128) == 0
+    assert f(7, 64, 8, 128) == 0
+
+
+def test_mxfp4_cache_rules(lib):
+    assert _decode(lib, _cache(cache_dtype=B.PKV_MXFP4, page_size=16), _seqs()) == B.PKV_EUNSUPPORTED
+    c = _cache(cache_dtype=B.PKV_MXFP4, page_size=32)
+    s = _seqs(max_pages=4, max_len=64)
+    assert _decode(lib, c, s, q_dtype=B.PKV_F32) == B.PKV_EUNSUPPORTED   # matrix-core path only
+    assert _decode(lib, c, s, hq=6) == B.PKV_EUNSUPPORTED                 # group 3
+    need = lib.paged_attn_decode_workspace_size(ctypes.byref(c), ctypes.byref(s), B.PKV_BF16, 4, 0)
+    assert need > 0
