@@ -41,6 +41,7 @@ WORKLOADS = {
     "fp8_shared_prefix_decode": 5,
     "spec_verify4_bf16": 6,
     "llama3_8b_decode_mxfp4": (2, {"kv_dtype": "mxfp4"}),
+    "mixed_inflight_mxfp4": (3, {"kv_dtype": "mxfp4"}),
 }
 
 
@@ -55,7 +56,8 @@ def kv_bytes_per_elem(kv_dtype: str) -> float:
     """Cache bytes per K or V element (MXFP4: half a byte plus a scale byte per 32)."""
     return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 17.0 / 32.0}[kv_dtype]
 # sources of the decode call on the matrix-core path (the traffic record is void once any changes)
-KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp")
+KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp",
+                  "../build.py")  # (the compile flags too)
 
 
 def kernel_source_hash() -> str:

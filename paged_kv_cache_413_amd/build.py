@@ -25,6 +25,15 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
+# Per-source device flags.  The decode kernels keep their MFMA operands and
+# accumulators in ordinary vector registers: the compiler's default puts the output
+# accumulator in AGPRs and then copies all of it to VGPRs and back around the
+# (rarely taken) online-softmax rescale of every block -- ~60 moves per block, which
+# the MXFP4 decode, bound by its vector work, cannot afford.  (The prefill source does
+# not compile with this option, and does not need it.)
+SOURCE_FLAGS = {
+    "attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _hipcc() -> str:
@@ -41,7 +50,7 @@ def sources():
 
 def _compile(hipcc, src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

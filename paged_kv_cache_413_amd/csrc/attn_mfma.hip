@@ -137,9 +137,18 @@ __device__ __forceinline__ void finish(const State<D>& st, const AttnArgs& a, in
 #endif
 constexpr int kWgWaves = PKV_DECODE_WG_WAVES;
 
+// Waves per SIMD the decode kernels are compiled for (bf16 / FP8: see
+// PKV_DECODE_WAVES_PER_EU).  MXFP4 does several times the vector work per byte; two
+// waves let one SIMD issue one wave's decoding while the other waits for its loads.
+#ifndef PKV_MX_WAVES_PER_EU
+#define PKV_MX_WAVES_PER_EU 2
+#endif
+template <int KV>
+constexpr int kDecodeWavesPerEu = KV == DT_MXFP4 ? PKV_MX_WAVES_PER_EU : PKV_DECODE_WAVES_PER_EU;
+
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
-__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_fixed_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<KV>, kDecodeWavesPerEu<KV>))) void decode_fixed_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = int64_t(blockIdx.x) * kWgWaves + uniform32(threadIdx.x >> 6);
   const int Hkv = a.cache.num_kv_heads;
@@ -234,7 +243,7 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, const i
 // cu_q_lens[s] + j at position L - nq + j, and records hold 16 rows.  Otherwise one
 // query per sequence (packed row s) and records of G rows.
 template <int KV, int D, int G, bool SMALLP, bool MQ>
-__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU, PKV_DECODE_WAVES_PER_EU))) void decode_auto_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<KV>, kDecodeWavesPerEu<KV>))) void decode_auto_kernel(AttnArgs a) {
   constexpr int ROWS = MQ ? 16 : G;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWgWaves + uniform32(threadIdx.x >> 6);

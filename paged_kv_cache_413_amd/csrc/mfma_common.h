@@ -47,9 +47,16 @@ constexpr int LOG2_BT = 5;
 #ifndef PKV_DECODE_WAVES_PER_EU
 #define PKV_DECODE_WAVES_PER_EU 1
 #endif
-// Blocks whose loads are in flight while one is folded, plus one (2 or 3 buffers).
+// Register buffers of the block pipeline (blocks in flight while one is folded, plus
+// one).  MXFP4 blocks (4.25 KiB per wave) are bound by their decoding, not by bytes in
+// flight: measured on the Llama batch, two buffers with two waves per SIMD take 41 us
+// per call; three or four buffers with two waves 42-43 us; one wave per SIMD 48-53 us
+// at any depth; three or four waves per SIMD spill registers (55-100 us).
 #ifndef PKV_DECODE_DEPTH
 #define PKV_DECODE_DEPTH 2
+#endif
+#ifndef PKV_MX_DEPTH
+#define PKV_MX_DEPTH 2
 #endif
 
 __device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -795,15 +802,17 @@ __device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&
 }
 
 // Blocks [b0, b1) of one (sequence, kv head), folded in order by fold(block, t0), all
-// of whose pages lie in the window `win` (unused with SMALLP).  PKV_DECODE_DEPTH
-// register buffers rotate: while block i is folded the loads of the next DEPTH-1
-// blocks are in flight.  Inside the loop every prefetch is unconditional, so each
-// fold waits only for its own block's loads (a partial vmcnt), never for prefetches
-// issued after them; the last blocks are peeled.
+// of whose pages lie in the window `win` (unused with SMALLP).  N register buffers
+// rotate: while block i is folded the loads of blocks i+1 .. i+N-1 are in flight.  The
+// steady state runs in rounds of N blocks (every buffer index a constant) whose
+// prefetches all lie in the range and are unconditional, so each fold waits only for
+// its own block's loads (a partial vmcnt), never for later prefetches; the last blocks
+// take a tail whose prefetches are guarded.
 template <int KV, int D, bool SMALLP, typename FoldFn>
 __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                                 const PageWindow& win, int b0, int b1, int L, int log2P,
                                                 int64_t kv_stride_b, int64_t head_off_b, int lane, FoldFn& fold) {
+  constexpr int N = KV == DT_MXFP4 ? PKV_MX_DEPTH : PKV_DECODE_DEPTH;
   const LaneOffsets lo = lane_offsets<KV, D>(lane);
   auto ld = [&](BlockOf<KV, D>& b, int blk) {
     if constexpr (KV == DT_MXFP4)
@@ -811,55 +820,30 @@ __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, c
     else
       load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
   };
-  BlockOf<KV, D> x, y;
-  ld(x, b0);
-  int blk = b0;
-  if constexpr (PKV_DECODE_DEPTH == 2) {
-    for (; blk + 2 < b1; blk += 2) {
-      ld(y, blk + 1);
-      fold(x, blk << LOG2_BT);
-      ld(x, blk + 2);
-      fold(y, (blk + 1) << LOG2_BT);
-    }
-    if (blk + 1 < b1) {
-      ld(y, blk + 1);
-      fold(x, blk << LOG2_BT);
-      fold(y, (blk + 1) << LOG2_BT);
-    } else {
-      fold(x, blk << LOG2_BT);
+  BlockOf<KV, D> buf[N];
+  const int nb = b1 - b0;
+  int i = 0;
+  if (nb >= 2 * N - 1) {
+#pragma unroll
+    for (int k = 0; k < N - 1; ++k) ld(buf[k], b0 + k);
+    for (; i + 2 * N - 1 <= nb; i += N) {
+#pragma unroll
+      for (int k = 0; k < N; ++k) {
+        ld(buf[(k + N - 1) % N], b0 + i + k + N - 1);
+        fold(buf[k], (b0 + i + k) << LOG2_BT);
+      }
     }
   } else {
-    BlockOf<KV, D> z;
-    if (b1 - b0 == 1) {
-      fold(x, blk << LOG2_BT);
-      return;
-    }
-    ld(y, b0 + 1);
-    for (; blk + 4 < b1; blk += 3) {
-      ld(z, blk + 2);
-      fold(x, blk << LOG2_BT);
-      ld(x, blk + 3);
-      fold(y, (blk + 1) << LOG2_BT);
-      ld(y, blk + 4);
-      fold(z, (blk + 2) << LOG2_BT);
-    }
-    const int r = b1 - blk;  // 2..4 blocks left; x and y hold blk, blk+1
-    if (r == 2) {
-      fold(x, blk << LOG2_BT);
-      fold(y, (blk + 1) << LOG2_BT);
-    } else if (r == 3) {
-      ld(z, blk + 2);
-      fold(x, blk << LOG2_BT);
-      fold(y, (blk + 1) << LOG2_BT);
-      fold(z, (blk + 2) << LOG2_BT);
-    } else {
-      ld(z, blk + 2);
-      fold(x, blk << LOG2_BT);
-      ld(x, blk + 3);
-      fold(y, (blk + 1) << LOG2_BT);
-      fold(z, (blk + 2) << LOG2_BT);
-      fold(x, (blk + 3) << LOG2_BT);
-    }
+#pragma unroll
+    for (int k = 0; k < N - 1; ++k)
+      if (k < nb) ld(buf[k], b0 + k);
+  }
+  // blocks i .. nb-1, fewer than 2N - 1; blocks i .. i+N-2 are loaded or in flight
+#pragma unroll
+  for (int k = 0; k < 2 * N - 1; ++k) {
+    if (i + k >= nb) break;
+    if (i + k + N - 1 < nb) ld(buf[(k + N - 1) % N], b0 + i + k + N - 1);
+    fold(buf[k % N], (b0 + i + k) << LOG2_BT);
   }
 }
 

@@ -10,7 +10,8 @@
 // products run on the MFMA units.  The 16 MFMA rows of a tile are 16/G consecutive
 // queries x the G heads of one kv head; a wave carries kPrefillTiles tiles, so every
 // K/V block it loads (one 32-token block, straight into operand registers, the same
-// loads as decode) feeds kPrefillTiles x 16 rows.  Causality is a per-row key limit,
+// loads as decode) feeds kPrefillTiles x 16 rows (this per-wave kernel serves pages of
+// fewer than 32 tokens and MXFP4 caches; other prefill runs on the LDS-shared kernel).  Causality is a per-row key limit,
 // applied only on the blocks that reach a row's position.
 //
 // Work item (one wave): (sequence, kv head, key split, query tile).  When the chunk
@@ -24,14 +25,18 @@
 namespace pkv {
 namespace {
 
-constexpr int kPrefillTiles = 4;  // 16-row tiles per wave
+// 16-row tiles per wave of the per-wave kernel: four for D = 64; two for D = 128, where
+// four tiles' accumulators, queries and two blocks in flight exceed the 256 vector
+// registers a wave can address and spill.
+template <int D>
+constexpr int kPrefillTiles = D == 128 ? 2 : 4;
 constexpr int kXcds = 8;
 
-// Query tile geometry for G query heads per kv head.
-template <int G>
+// Query tile geometry for G query heads per kv head (per-wave kernel: D's tile count).
+template <int G, int D = 64>
 struct PfGeom {
-  static constexpr int QPT = 16 / G;                 // queries per 16-row tile
-  static constexpr int QW = kPrefillTiles * QPT;     // queries per wave
+  static constexpr int QPT = 16 / G;                    // queries per 16-row tile
+  static constexpr int QW = kPrefillTiles<D> * QPT;     // queries per wave
 };
 
 // Finish the NT row tiles of a wave: rows of the chunk only.  One split: output and
@@ -86,7 +91,7 @@ __device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D>
 
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(AttnArgs a) {
-  constexpr int NT = kPrefillTiles, QPT = PfGeom<G>::QPT, QW = PfGeom<G>::QW;
+  constexpr int NT = kPrefillTiles<D>, QPT = PfGeom<G, D>::QPT, QW = PfGeom<G, D>::QW;
   const int lane = threadIdx.x, n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
   const int QT = a.pf_qtiles;
@@ -537,7 +542,7 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
                            int* resident_items) {
   const bool lds = page_size >= BT && kv_dtype != DT_MXFP4;
-  *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : kPrefillTiles);
+  *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : head_dim == 128 ? kPrefillTiles<128> : kPrefillTiles<64>);
   const void* k;
   if (kv_dtype == DT_MXFP4) {
     k = head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 64, 4, false>)
