@@ -52,6 +52,13 @@ def make_workload(name: str, **over):
     return workloads.make(cfg, **{**base, **over})
 
 
+def compute_dtype(wl) -> str:
+    """Arithmetic type of the attention products: fp32 for fp32 caches, else bf16 MFMA
+    with fp32 accumulation (FP8 and MXFP4 values are decoded to bf16 exactly; the cache
+    format is config.kv_dtype)."""
+    return "f32" if wl.kv_dtype == "f32" else "bf16"
+
+
 def kv_bytes_per_elem(kv_dtype: str) -> float:
     """Cache bytes per K or V element (MXFP4: half a byte plus a scale byte per 32)."""
     return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 17.0 / 32.0}[kv_dtype]
@@ -333,7 +340,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.kv_dtype,
+        "dtype": compute_dtype(wl),
         "data": "synthetic (seeded N(0,1) K/V/Q, seeded lengths and page permutation)",
         "config": {"workload": wl.name, "num_seqs": wl.num_seqs, "num_prefill": wl.num_prefill,
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads,
