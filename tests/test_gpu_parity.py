@@ -47,6 +47,33 @@ def test_append_is_bit_exact(gpu_lib, name):
         f"{int((got.view(np.uint8) != ref.view(np.uint8)).sum())} bytes differ"
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_append_routes_rows_across_many_sequences(gpu_lib, kv):
+    """kv_append over 300 sequences (more than one workgroup samples at once, so the row
+    owner is found in two rounds) where only every third sequence has a new row: each
+    row lands in its own sequence's slot and sequences without rows keep their bytes."""
+    from paged_kv_cache_413_amd import binding as B
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch, to_device
+    wl = workloads.make(2, num_seqs=300, len_range=(2, 90), kv_dtype=kv)
+    print(f"[case] sparse append S={wl.num_seqs} kv={kv}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    new = (np.arange(wl.num_seqs) % 3 == 1).astype(np.int32)
+    k, v = wl.step_kv()  # one row per sequence; keep those of the sequences that append
+    k, v = k[new == 1], v[new == 1]
+    seqs = B.make_seqs(db.block_tables, db.context_lens, wl.max_context_len)
+    cu = torch.from_numpy(wl.cu(new)).to(db.dev)
+    B.kv_append(db.cache, seqs, to_device(k, wl.in_dtype, db.dev), to_device(v, wl.in_dtype, db.dev),
+                cu, int(new.sum()))
+    torch.cuda.synchronize()
+    ref = oracle_pool(wl, include_step=False)
+    kinv, vinv = wl.fp8_scales()[2:] if kv == "fp8" else (None, None)
+    oracle.append(ref, wl.block_tables, wl.context_lens, new, k, v, wl.in_dtype, wl.kv_dtype, kinv, vinv)
+    got = pool_token_major(db.pool_bits())
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), \
+        f"{int((got.view(np.uint8) != ref.view(np.uint8)).sum())} bytes differ"
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_debug_gather_is_bit_exact(gpu_lib, name):
     from paged_kv_cache_413_amd import binding as B
