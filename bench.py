@@ -124,9 +124,12 @@ def algorithmic_bytes(wl) -> dict:
 
 
 def cpu_baseline(wl, budget_s: float):
-    """The CPU fp64 oracle on a bounded sample of the workload's decode sequences:
-    this step's append into an oracle pool holding those sequences' history, then
-    their decode attention.  Returns the dict for the JSON line."""
+    """The CPU fp64 oracle on a bounded sample of the workload's attention rows: this
+    step's append into an oracle pool holding a sequence's history, then its attention.
+    Sequences are taken in order until budget_s seconds of oracle work; when the whole
+    workload takes less, the timed calls repeat over the sequences whose pools were
+    kept (up to 2 GB of pools) until the budget is spent.  Returns the dict for the
+    JSON line."""
     import numpy as np
     import oracle
 
@@ -140,22 +143,11 @@ def cpu_baseline(wl, budget_s: float):
     q_all = wl.q_packed()
     cu = wl.cu(wl.new_lens)
     elem = kv_bytes_per_elem(wl.kv_dtype)
-    done, bytes_done, t_spent = [], 0, 0.0
-    for s in order:
-        # a compact pool holding sequence s's pages only, with its table renumbered
-        # (the oracle's result does not depend on physical page ids)
-        row = wl.block_tables[s]
-        used = row[row >= 0]
-        table = np.full((1, len(row)), -1, np.int32)
-        table[0, :len(used)] = np.arange(len(used), dtype=np.int32)
-        pool = oracle.new_pool(len(used), wl.num_kv_heads, wl.page_size, wl.head_dim,
-                               wl.kv_dtype, fill=poison)
+
+    def timed(s, pool, table):
+        # the step's append (idempotent: it rewrites the same slots) and the attention
         L, n = int(wl.context_lens[s]), int(wl.new_lens[s])
-        k_hist, v_hist = wl.tokens(s, 0, L - n)
         rows = np.array([s])
-        if L - n:
-            oracle.append(pool, table, np.array([L - n]), np.array([L - n]),
-                          k_hist, v_hist, wl.in_dtype, wl.kv_dtype, kinv, vinv)
         k_new, v_new = wl.tokens(s, L - n, L)
         q = q_all[cu[s]:cu[s + 1]]
         t0 = time.perf_counter()
@@ -167,18 +159,47 @@ def cpu_baseline(wl, budget_s: float):
         else:
             oracle.decode(pool, table, wl.context_lens[rows], q, wl.q_dtype,
                           wl.sm_scale, wl.kv_dtype, ks, vs, window=wl.window)
-        t_spent += time.perf_counter() - t0
-        done.append(s)
-        bytes_done += (L - (max(0, L - n - wl.window + 1) if wl.window > 0 else 0)) * 2 * wl.num_kv_heads * wl.head_dim * elem
-        del pool
+        dt = time.perf_counter() - t0
+        kv = (L - (max(0, L - n - wl.window + 1) if wl.window > 0 else 0)) * 2 * wl.num_kv_heads * wl.head_dim * elem
+        return dt, kv
+
+    calls, bytes_done, t_spent, kept, kept_bytes = 0, 0, 0.0, [], 0
+    for s in order:
+        # a compact pool holding sequence s's pages only, with its table renumbered
+        # (the oracle's result does not depend on physical page ids)
+        row = wl.block_tables[s]
+        used = row[row >= 0]
+        table = np.full((1, len(row)), -1, np.int32)
+        table[0, :len(used)] = np.arange(len(used), dtype=np.int32)
+        pool = oracle.new_pool(len(used), wl.num_kv_heads, wl.page_size, wl.head_dim,
+                               wl.kv_dtype, fill=poison)
+        L, n = int(wl.context_lens[s]), int(wl.new_lens[s])
+        if L - n:
+            k_hist, v_hist = wl.tokens(s, 0, L - n)
+            oracle.append(pool, table, np.array([L - n]), np.array([L - n]),
+                          k_hist, v_hist, wl.in_dtype, wl.kv_dtype, kinv, vinv)
+        dt, kv = timed(s, pool, table)
+        t_spent, bytes_done, calls = t_spent + dt, bytes_done + kv, calls + 1
+        if kept_bytes + pool.nbytes <= 2e9:
+            kept.append((s, pool, table))
+            kept_bytes += pool.nbytes
+        else:
+            del pool
         if t_spent >= budget_s:
             break
+    seqs_sampled = calls
+    while t_spent < budget_s and kept:
+        for s, pool, table in kept:
+            dt, kv = timed(s, pool, table)
+            t_spent, bytes_done, calls = t_spent + dt, bytes_done + kv, calls + 1
+            if t_spent >= budget_s:
+                break
     gbs = bytes_done / t_spent / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": (f"{len(done)} of {len(order)} {'chunk' if prefill_only else 'decode'} sequences of "
-                       f"{wl.name} ({bytes_done / 1e6:.1f} MB of KV, {t_spent:.1f} s): kv_append of the "
-                       f"step's tokens then fp64 {'causal chunk' if prefill_only else 'decode'} attention, "
-                       f"history preloaded untimed"),
+            "sample": (f"{seqs_sampled} of {len(order)} {'chunk' if prefill_only else 'decode'} sequences of "
+                       f"{wl.name}, {calls} timed sequence calls ({bytes_done / 1e6:.1f} MB of KV, "
+                       f"{t_spent:.1f} s): kv_append of the step's tokens then fp64 "
+                       f"{'causal chunk' if prefill_only else 'decode'} attention, history preloaded untimed"),
             "seconds": round(t_spent, 3)}
 
 

@@ -41,15 +41,20 @@ def test_full_size_sampled_rows(gpu_lib, cfg, over):
     rng = np.random.default_rng(cfg)
     while len(picks) < min(SAMPLES[cfg], wl.num_seqs - npf):
         picks.add(int(rng.integers(npf, wl.num_seqs)))
+    err = {"decode": 0.0, "prefill": 0.0, "lse": 0.0}
     for s in sorted(picks):
         ref_o, ref_l = oracle_sequence(wl, s)
         r = s - npf
-        assert_close(dec[r:r + 1], ref_o, wl.kv_dtype, f"{wl.name} seq {s}")
-        assert_lse_close(dec_lse[r:r + 1], ref_l, wl.kv_dtype, f"{wl.name} seq {s}")
+        err["decode"] = max(err["decode"], assert_close(dec[r:r + 1], ref_o, wl.kv_dtype, f"{wl.name} seq {s}"))
+        err["lse"] = max(err["lse"], assert_lse_close(dec_lse[r:r + 1], ref_l, wl.kv_dtype, f"{wl.name} seq {s}"))
     cu = wl.cu(wl.new_lens)
     pf_picks = range(npf) if npf <= 8 else sorted(set(np.random.default_rng(cfg + 100).integers(0, npf, 6).tolist()))
     for s in pf_picks:
         ref_o, ref_l = oracle_sequence(wl, s)
-        assert_close(pf[cu[s]:cu[s + 1]], ref_o, wl.kv_dtype, f"{wl.name} prefill {s}")
-        assert_lse_close(pf_lse[cu[s]:cu[s + 1]], ref_l, wl.kv_dtype, f"{wl.name} prefill {s}")
-    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {len(pf_picks)} prefill requests", flush=True)
+        err["prefill"] = max(err["prefill"], assert_close(pf[cu[s]:cu[s + 1]], ref_o, wl.kv_dtype,
+                                                          f"{wl.name} prefill {s}"))
+        err["lse"] = max(err["lse"], assert_lse_close(pf_lse[cu[s]:cu[s + 1]], ref_l, wl.kv_dtype,
+                                                      f"{wl.name} prefill {s}"))
+    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {len(pf_picks)} prefill requests; largest "
+          f"errors ({'abs' if wl.kv_dtype == 'f32' else 'rel'}) decode {err['decode']:.2e}, "
+          f"prefill {err['prefill']:.2e}, lse (abs) {err['lse']:.2e}", flush=True)
