@@ -234,6 +234,24 @@ def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
     assert_lse_close(lse, ref[1], "bf16", f"P={P}")
 
 
+@pytest.mark.parametrize("kv,num_seqs,splits", [("bf16", 3000, 0), ("bf16", 3000, 2), ("fp8", 1000, 0)])
+def test_many_short_sequences(gpu_lib, kv, num_seqs, splits):
+    """Thousands of decode sequences of 1..80 tokens (Llama-3-8B heads, pages of 64):
+    the balanced schedule's search over sequences runs many 64-sequence rounds and its
+    shares hold many whole segments; fixed partitions give most sequences one."""
+    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    wl = workloads.make(2, num_seqs=num_seqs, len_range=(1, 80), kv_dtype=kv, num_splits=splits)
+    print(f"[case] many sequences S={num_seqs} kv={kv} splits={splits}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.step()
+    torch.cuda.synchronize()
+    dec, lse, _, _ = db.outputs_f64()
+    ref = oracle_outputs(wl, oracle_pool(wl))
+    assert_close(dec, ref[0], kv, f"S={num_seqs}")
+    assert_lse_close(lse, ref[1], kv, f"S={num_seqs}")
+
+
 AUTO_WAVES = [
     # (waves, workload, overrides): few waves, so shares are long and spread over
     # several (sequence, kv head) segments, and segments over several waves
