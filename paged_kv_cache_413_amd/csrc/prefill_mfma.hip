@@ -11,7 +11,7 @@
 // queries x the G heads of one kv head; a wave carries kPrefillTiles tiles, so every
 // K/V block it loads (one 32-token block, straight into operand registers, the same
 // loads as decode) feeds kPrefillTiles x 16 rows (this per-wave kernel serves pages of
-// fewer than 32 tokens and MXFP4 caches; other prefill runs on the LDS-shared kernel).  Causality is a per-row key limit,
+// fewer than 32 tokens; other prefill runs on the LDS-shared kernel).  Causality is a per-row key limit,
 // applied only on the blocks that reach a row's position.
 //
 // Work item (one wave): (sequence, kv head, key split, query tile).  When the chunk
@@ -195,7 +195,7 @@ constexpr int kPfStages = 3;
 
 template <int KV, int D>
 struct PfStage {
-  static constexpr int esz = KV == DT_BF16 ? 2 : 1;
+  static constexpr int esz = KV == DT_FP8 ? 1 : 2;  // MXFP4 blocks are staged decoded, as bf16
   static constexpr int KCHUNK = BT * 32 * esz;   // one 32-dim chunk of the block's K
   static constexpr int KBYTES = D * BT * esz;
   static constexpr int BYTES = 2 * KBYTES;       // K and V of one block
@@ -203,6 +203,25 @@ struct PfStage {
   static constexpr int PIECES = BYTES / 1024;    // 1 KiB pieces, one per wave-wide 16-B load
   static constexpr int PER_WAVE = (PIECES + kPfWaves - 1) / kPfWaves;
   static constexpr bool EVEN = PIECES % kPfWaves == 0;  // else waves >= PIECES copy nothing
+};
+
+// Codes 2w, 2w+1 (byte w) of an E2M1 word times `scale`, as two bf16 (low: code 2w).
+__device__ __forceinline__ uint32_t fp4_pair_to_bf16(uint32_t codes, float scale, int w) {
+  switch (w) {  // the byte select is an immediate
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  }
+}
+
+// One thread's fetched share of an MXFP4 block (prefill_lds_kernel): a K code word
+// and its scale byte, a V code word and the scale words of its 8 positions (S = 8 for
+// D = 128: one word per position; 4 for D = 64: one word per two positions).
+template <int S>
+struct MxSlot {
+  uint32_t kw, ks, vw;
+  uint32_t vs[S];
 };
 
 // Workgroup barrier; LDS writes and reads of this wave are complete before it.
@@ -216,7 +235,7 @@ __device__ __forceinline__ void stage_barrier() {
 template <int KV>
 __device__ __forceinline__ bf16x8 lds8(const char* p) {
   Frag8 f;
-  if constexpr (KV == DT_BF16) {
+  if constexpr (KV != DT_FP8) {  // bf16 stages (MXFP4 blocks are staged decoded)
     f.q = *reinterpret_cast<const uint4*>(p);
   } else {
     const uint2 w = *reinterpret_cast<const uint2*>(p);
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   for (int r = 0; r < NT; ++r) state_init(st[r]);
 
   const int log2P = a.cache.log2_page, P = 1 << log2P;
-  const int64_t tile_b = int64_t(P) * D * esz, kv_stride_b = Hkv * tile_b, head_off_b = g * tile_b;
+  const int64_t tile_b = tile_bytes(KV, P, D), kv_stride_b = Hkv * tile_b, head_off_b = g * tile_b;
   const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
   const char* pool = static_cast<const char*>(a.cache.pool);
   // this thread's 16-byte share of each of this wave's PER_WAVE pieces of a block
@@ -368,6 +387,81 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     }
   };
 
+  // MXFP4: a thread fetches the codes of 8 dims of one token row of K (one word) with
+  // its scale byte, and of 8 positions of one dim of V (one word) with the scale
+  // words of those positions (one per position: its D/32 block scales); staging
+  // decodes them to the bf16 stage layout above (K: code x block scale; V: each
+  // position with its own scale), so the workgroup decodes every block once and the
+  // waves read bf16 operands.  D = 128: every thread has one K and one V word; D = 64:
+  // the first 256 threads.
+  constexpr int MXK = 32 * D / 8, MXV = 4 * D, MXS = D / 32 >= 4 ? 8 : 4;  // items; scale words of a V item
+  auto fetch_mx = [&](MxSlot<MXS>& r, int blk) {
+    if constexpr (KV == DT_MXFP4) {
+      const int t = blk << LOG2_BT;
+      typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+      const int32_t page = ((const_i32_ptr)(uintptr_t)bt)[t >> log2P];
+      const uint32_t slot0 = uint32_t(t & (P - 1)), tb = uint32_t(tile_b);
+      const char* Kt = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
+      const auto rk = tile_rsrc(Kt, tb);
+      const auto rv = tile_rsrc(Kt + kv_stride_b, tb);
+      const uint32_t codes = uint32_t(P) * (D / 2);
+      if (tid < MXK) {
+        const int tk = tid >> 4, j = (tid & 15) >> 2, cc = tid & 3;
+        const uint32_t row = slot0 + uint32_t(tk);
+        r.kw = __builtin_amdgcn_raw_buffer_load_b32(rk, row * (D / 2) + 4 * (cc * (D / 32) + j), 0, 0);
+        r.ks = __builtin_amdgcn_raw_buffer_load_b8(rk, codes + row * (D / 32) + j, 0, 0);
+      }
+      if (tid < MXV) {
+        const int d = tid >> 2, cc = tid & 3, m = d & 15, u = d >> 4;
+        const uint32_t sb = slot0 >> 5;
+        r.vw = __builtin_amdgcn_raw_buffer_load_b32(rv, sb * 16 * D + 4 * ((4 * m + cc) * (D / 16) + u), 0, 0);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const uint32_t so = codes + (sb * 32 + 8 * cc) * (D / 32);  // positions 8cc .. 8cc+7
+#pragma unroll
+        for (int h = 0; h < MXS / 4; ++h) {
+          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, so + 16 * h, 0, 0));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) r.vs[4 * h + k] = v[k];
+        }
+      }
+    }
+  };
+  auto stash_mx = [&](MxSlot<MXS>& r, int stage, int blk) {
+    if constexpr (KV == DT_MXFP4) {
+      char* dst = smem + stage * SL::BYTES;
+      const int nvalid = L - (blk << LOG2_BT);
+      if (tid < MXK) {
+        const int tk = tid >> 4, j = (tid & 15) >> 2, cc = tid & 3;
+        Frag8 f;
+        f.v = fp4x8_to_bf16(r.kw, e8m0_value(r.ks & 255u));
+        *reinterpret_cast<uint4*>(dst + j * SL::KCHUNK + tk * 64 + 16 * (cc ^ ((tk >> 1) & 3))) = f.q;
+      }
+      if (tid < MXV) {
+        const int d = tid >> 2, cc = tid & 3, j = d >> 5;
+        Frag8 f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // positions 8cc + 2w, +1: each code with its own scale
+          uint32_t h[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int e = 2 * w + k, byte = e * (D / 32) + j;  // scale of position 8cc + e, block j
+            const float sc = e8m0_value((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u);
+            const uint32_t x = fp4_pair_to_bf16(r.vw, sc, w);
+            h[k] = tok_of(cc, e) < nvalid ? (k ? (x >> 16) : (x & 0xffffu)) : 0u;  // V past the end: 0
+          }
+          f.w[w] = h[0] | (h[1] << 16);
+        }
+        *reinterpret_cast<uint4*>(dst + SL::KBYTES + d * 64 + 16 * (cc ^ ((d >> 1) & 3))) = f.q;
+      }
+    }
+  };
+  auto fetch_any = [&](auto& r, int blk) {
+    if constexpr (KV == DT_MXFP4) fetch_mx(r, blk); else fetch(r, blk);
+  };
+  auto stash_any = [&](auto& r, int stage, int blk) {
+    if constexpr (KV == DT_MXFP4) stash_mx(r, stage, blk); else stash(r, stage, blk);
+  };
+
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
   const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3))) : uint32_t(n * 32 + 8 * c);
@@ -394,13 +488,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   // P.V products of block i -- is one straight-line stretch in which the scheduler
   // interleaves the matrix-core and vector instructions.
   const int last = b1 - 1;
-  uint4 ra[SL::PER_WAVE], rb[SL::PER_WAVE];
+  std::conditional_t<KV == DT_MXFP4, MxSlot<MXS>, uint4[SL::PER_WAVE]> ra, rb;
   float sa_[NT][8], sb_[NT][8];
-  auto step = [&](uint4 (&rs)[SL::PER_WAVE], int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
+  auto step = [&](auto& rs, int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
     const int t = (b0 + i) << LOG2_BT;
     const int blk2 = min(b0 + i + 2, last);
-    stash(rs, (i + 2) % kPfStages, blk2);
-    fetch(rs, min(b0 + i + 4, last));
+    stash_any(rs, (i + 2) % kPfStages, blk2);
+    fetch_any(rs, min(b0 + i + 4, last));
     if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
       for (int r = 0; r < NT; ++r)
@@ -434,12 +528,12 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     stage_barrier();
   };
   if (nblk > 0) {
-    fetch(ra, b0);
-    fetch(rb, min(b0 + 1, last));
-    stash(ra, 0, b0);
-    fetch(ra, min(b0 + 2, last));
-    stash(rb, 1, min(b0 + 1, last));
-    fetch(rb, min(b0 + 3, last));
+    fetch_any(ra, b0);
+    fetch_any(rb, min(b0 + 1, last));
+    stash_any(ra, 0, b0);
+    fetch_any(ra, min(b0 + 2, last));
+    stash_any(rb, 1, min(b0 + 1, last));
+    fetch_any(rb, min(b0 + 3, last));
     stage_barrier();
     scores(0, sa_);
   }
@@ -498,7 +592,7 @@ template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int groups = a.seqs.num_seqs * a.cache.num_kv_heads * a.max_splits;
   const int64_t grid = int64_t((groups + kXcds - 1) / kXcds) * kXcds * a.pf_qtiles;
-  if constexpr (SMALLP || KV == DT_MXFP4) {  // one wave per item (MXFP4: pages of >= 32 tokens)
+  if constexpr (SMALLP) {  // one wave per item (pages of fewer than 32 tokens)
     hipLaunchKernelGGL((prefill_kernel<KV, D, G, SMALLP>), dim3(unsigned(grid)), dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((prefill_lds_kernel<KV, D, G>), dim3(unsigned(grid)), dim3(64 * kPfWaves), 0, st, a);
@@ -541,12 +635,12 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 
 void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
                            int* resident_items) {
-  const bool lds = page_size >= BT && kv_dtype != DT_MXFP4;
+  const bool lds = page_size >= BT;
   *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : head_dim == 128 ? kPrefillTiles<128> : kPrefillTiles<64>);
   const void* k;
   if (kv_dtype == DT_MXFP4) {
-    k = head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 64, 4, false>)
-                       : reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 128, 4, false>);
+    k = head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 64, 4>)
+                       : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 128, 4>);
   } else if (lds) {
     k = kv_dtype == DT_BF16
             ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 64, 4>)
