@@ -42,6 +42,7 @@ WORKLOADS = {
     "spec_verify4_bf16": 6,
     "llama3_8b_decode_mxfp4": (2, {"kv_dtype": "mxfp4"}),
     "mixed_inflight_mxfp4": (3, {"kv_dtype": "mxfp4"}),
+    "mixed_inflight_fp8": (3, {"kv_dtype": "fp8"}),
 }
 
 

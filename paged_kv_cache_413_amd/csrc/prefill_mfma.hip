@@ -175,8 +175,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // 16-byte pieces of it into registers four blocks ahead (two register slots), then
 // writes them into one of three LDS stages two blocks ahead -- and each wave reads its
 // MFMA operands from the stage with the same lane offsets as from the tile in HBM.  The
-// stage layout mirrors the block's HBM layout: K as D/32 chunks of [32 tokens][32
-// dims], then V as [D][32 positions].  Three stages let a wave compute the scores of
+// stage layout mirrors the block's HBM layout, in bf16: K as D/32 chunks of [32 tokens]
+// [32 dims], then V as [D][32 positions].  FP8 and MXFP4 blocks are decoded to bf16 as
+// they are staged, once per workgroup rather than once per wave that reads them (twice
+// the LDS bytes of an FP8 stage, a sixth of the conversions).  Three stages let a wave compute the scores of
 // block i+1 (matrix cores) while it runs the softmax of block i (vector ALU) and then
 // the P.V products of block i: the two units work at once within each wave, instead
 // of every wave waiting on one then the other between barriers.
@@ -195,12 +197,17 @@ constexpr int kPfStages = 3;
 
 template <int KV, int D>
 struct PfStage {
-  static constexpr int esz = KV == DT_FP8 ? 1 : 2;  // MXFP4 blocks are staged decoded, as bf16
+  // stages hold bf16: FP8 and MXFP4 blocks are decoded once, as they are staged
+  static constexpr int esz = 2;
   static constexpr int KCHUNK = BT * 32 * esz;   // one 32-dim chunk of the block's K
   static constexpr int KBYTES = D * BT * esz;
   static constexpr int BYTES = 2 * KBYTES;       // K and V of one block
-  static constexpr int KPIECES = KBYTES / 1024;
-  static constexpr int PIECES = BYTES / 1024;    // 1 KiB pieces, one per wave-wide 16-B load
+  // fetch geometry of bf16 / FP8 tiles (MXFP4 has its own): 1 KiB pieces of the tile,
+  // one per wave-wide 16-byte load
+  static constexpr int fsz = KV == DT_FP8 ? 1 : 2;
+  static constexpr int FKCHUNK = BT * 32 * fsz;
+  static constexpr int KPIECES = D * BT * fsz / 1024;
+  static constexpr int PIECES = 2 * KPIECES;
   static constexpr int PER_WAVE = (PIECES + kPfWaves - 1) / kPfWaves;
   static constexpr bool EVEN = PIECES % kPfWaves == 0;  // else waves >= PIECES copy nothing
 };
@@ -235,15 +242,7 @@ __device__ __forceinline__ void stage_barrier() {
 template <int KV>
 __device__ __forceinline__ bf16x8 lds8(const char* p) {
   Frag8 f;
-  if constexpr (KV != DT_FP8) {  // bf16 stages (MXFP4 blocks are staged decoded)
-    f.q = *reinterpret_cast<const uint4*>(p);
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
-    f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
-    f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
-    f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
-  }
+  f.q = *reinterpret_cast<const uint4*>(p);  // every stage holds bf16
   return f.v;
 }
 
@@ -315,7 +314,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
     const int32_t page = ((const_i32_ptr)(uintptr_t)bt)[t >> log2P];
     const uint32_t slot0 = uint32_t(t & (P - 1));
-    const uint32_t tile_bytes = uint32_t(P) * D * esz;
+    const uint32_t tile_bytes = uint32_t(P) * D * SL::fsz;
     const char* Kt = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
     const auto rk = tile_rsrc(Kt, tile_bytes);
     const auto rv = tile_rsrc(Kt + kv_stride_b, tile_bytes);
@@ -329,11 +328,11 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       u32x4 v;
       if (is_k) {
         const int off = p * 1024;
-        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t(off / SL::KCHUNK) * P + slot0) * 32 * esz +
-                                                           uint32_t(off % SL::KCHUNK));
+        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t(off / SL::FKCHUNK) * P + slot0) * 32 * SL::fsz +
+                                                           uint32_t(off % SL::FKCHUNK));
         v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * 16, so, 0));
       } else {
-        const uint32_t so = __builtin_amdgcn_readfirstlane(slot0 * D * esz + uint32_t(p - SL::KPIECES) * 1024);
+        const uint32_t so = __builtin_amdgcn_readfirstlane(slot0 * D * SL::fsz + uint32_t(p - SL::KPIECES) * 1024);
         v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16, so, 0));
       }
       r[k] = make_uint4(v[0], v[1], v[2], v[3]);
@@ -346,8 +345,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   // (two per window position), and the map spreads them over all of it (measured
   // conflict-free; the plain layout costs 4 extra cycles per read).  The copy writes
   // and the operand reads apply the same map.
-  const uint32_t wofs = esz == 2 ? uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 3) & 3)))
-                                 : uint32_t(lane * 16);
+  const uint32_t wofs = uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 3) & 3)));
   // Stage a block; in the sequence's last, partial block the V slots past its end are
   // zeroed here (they may hold anything, NaN included, and a zero weight would not
   // cancel a NaN), so the operand reads need no tail test.  The lane's 16 bytes are
@@ -364,7 +362,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           uint32_t keep = 0;
-          if constexpr (esz == 2) {
+          if constexpr (SL::fsz == 2) {
             const int p0 = 8 * (lane & 3) + 2 * j;
             keep = (tok_of(p0 >> 3, p0 & 7) < nvalid ? 0x0000ffffu : 0u) |
                    (tok_of((p0 + 1) >> 3, (p0 + 1) & 7) < nvalid ? 0xffff0000u : 0u);
@@ -382,8 +380,27 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     }
 #pragma unroll
     for (int k = 0; k < SL::PER_WAVE; ++k) {
-      if (!SL::EVEN && w + k * kPfWaves >= SL::PIECES) break;
-      *reinterpret_cast<uint4*>(dst + (w + k * kPfWaves) * 1024 + wofs) = r[k];
+      const int p = w + k * kPfWaves;
+      if (!SL::EVEN && p >= SL::PIECES) break;
+      if constexpr (SL::fsz == 2) {
+        *reinterpret_cast<uint4*>(dst + p * 1024 + wofs) = r[k];
+      } else {
+        // an FP8 piece is 32 rows of 32 codes (K: the tokens of one 32-dim chunk; V: 32
+        // dims); the lane's 16 codes (row lane/2, half lane&1) become 32 bytes of bf16,
+        // segments 2(lane&1) and 2(lane&1)+1 of that row of the stage
+        const int row = lane >> 1, s0 = 2 * (lane & 1), swz = (row >> 1) & 3;
+        char* base = dst + (p < SL::KPIECES ? p * SL::KCHUNK : SL::KBYTES + (p - SL::KPIECES) * 32 * 64) + row * 64;
+        const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          Frag8 f;
+          f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h], 1.0f, false));
+          f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h], 1.0f, true));
+          f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h + 1], 1.0f, false));
+          f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h + 1], 1.0f, true));
+          *reinterpret_cast<uint4*>(base + 16 * ((s0 + h) ^ swz)) = f.q;
+        }
+      }
     }
   };
 
@@ -464,7 +481,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
 
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
-  const uint32_t lk = esz == 2 ? uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3))) : uint32_t(n * 32 + 8 * c);
+  const uint32_t lk = uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3)));
   // Raw scores of block b0+i (stage i%3) for the wave's tiles.
   auto scores = [&](int i, float (&sc)[NT][8]) {
     const char* stg = smem + (i % kPfStages) * SL::BYTES;

@@ -17,9 +17,10 @@ pytestmark = pytest.mark.gpu
 
 SAMPLES = {1: 4, 2: 6, 3: 6, 4: 2, 5: 6, 6: 6}
 
-# (workload, overrides): the six workloads, and the Llama batch and the mixed batch with
-# an MXFP4 cache (the benchmark's MXFP4 lines)
-CASES = [(c, {}) for c in (1, 2, 3, 4, 5, 6)] + [(2, {"kv_dtype": "mxfp4"}), (3, {"kv_dtype": "mxfp4"})]
+# (workload, overrides): the six workloads, the Llama batch and the mixed batch with an
+# MXFP4 cache, and the mixed batch with an FP8 cache (the benchmark's other lines)
+CASES = [(c, {}) for c in (1, 2, 3, 4, 5, 6)] + [(2, {"kv_dtype": "mxfp4"}), (3, {"kv_dtype": "mxfp4"}),
+                                                 (3, {"kv_dtype": "fp8"})]
 
 
 @pytest.mark.parametrize("cfg,over", CASES, ids=lambda x: str(x) if isinstance(x, int) else (x.get("kv_dtype") or "-"))
