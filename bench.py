@@ -15,6 +15,8 @@ time over K uninstrumented steps.  Then each call of the step runs K times back 
 between two HIP events on the launch stream: `kernel_us` lists the mean duration of
 each call, and `roofline` rates the dominant one, paged_attn_decode (its attention
 kernel plus its merge kernel), against MI355X's 8 TB/s HBM peak.
+`kernel_us_cold_caches` gives the attention calls again, each alone after a 1 GiB write
+that evicts L2 and the Infinity Cache (median of K).
 `cpu_baseline` is the CPU fp64 oracle timed on a bounded sample of the same workload
 on the host cores.
 """
@@ -335,6 +337,27 @@ def main():
     append_us = per_call_us(db.append_step)
     prefill_us = per_call_us(db.prefill_step) if wl.num_prefill else None
     decode_us = per_call_us(db.decode_step) if wl.num_prefill < wl.num_seqs else None
+
+    # the same calls with cold caches: before each timed call a 1 GiB buffer is written
+    # (more than the 8 x 4 MB of L2 and the 256 MB Infinity Cache), then the call runs
+    # alone between two events; the median of K such calls
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def cold_call_us(fn):
+        ts = []
+        for _ in range(K):
+            flush.fill_(1)
+            a, b = E(enable_timing=True), E(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        return float(np.median(ts))
+
+    cold = {"paged_attn_prefill_chunk": round(cold_call_us(db.prefill_step), 2) if wl.num_prefill else None,
+            "paged_attn_decode": round(cold_call_us(db.decode_step), 2) if wl.num_prefill < wl.num_seqs else None}
+    del flush
     fmt = lambda us: "-" if us is None else f"{us:.1f} us"
     print(f"[bench] step {ms_step * 1e3:.1f} us; per call: append {append_us:.1f} us, prefill "
           f"{fmt(prefill_us)}, decode {fmt(decode_us)}", file=sys.stderr, flush=True)
@@ -375,6 +398,7 @@ def main():
         "kernel_us": {"kv_append": round(append_us, 2),
                       "paged_attn_prefill_chunk": None if prefill_us is None else round(prefill_us, 2),
                       "paged_attn_decode": None if decode_us is None else round(decode_us, 2)},
+        "kernel_us_cold_caches": cold,
         "roofline": {"bound": "hbm", "kernel": call,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
