@@ -119,8 +119,11 @@ def make_cache(pool: torch.Tensor, page_size: int, num_kv_heads: int, head_dim: 
     """Describe a pool tensor [num_pages][2][num_kv_heads][page_size][head_dim] (an MXFP4
     pool: uint8 [num_pages][2][num_kv_heads][tile bytes])."""
     assert pool.is_contiguous() and pool.dim() == (4 if cache_dtype == PKV_MXFP4 else 5)
-    return PkvCache(_ptr(pool), pool.shape[0], page_size, num_kv_heads, head_dim, cache_dtype,
-                    _ptr(k_scale), _ptr(v_scale), _ptr(k_inv_scale), _ptr(v_inv_scale))
+    c = PkvCache(_ptr(pool), pool.shape[0], page_size, num_kv_heads, head_dim, cache_dtype,
+                 _ptr(k_scale), _ptr(v_scale), _ptr(k_inv_scale), _ptr(v_inv_scale))
+    # the struct holds raw device pointers: keep the tensors alive as long as it lives
+    c._tensors = (pool, k_scale, v_scale, k_inv_scale, v_inv_scale)
+    return c
 
 
 def make_seqs(block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
@@ -130,9 +133,11 @@ def make_seqs(block_tables: torch.Tensor, context_lens: torch.Tensor, max_contex
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     assert block_tables.is_contiguous() and context_lens.is_contiguous()
     S = context_lens.shape[0]
-    return PkvSeqs(_ptr(block_tables), _ptr(context_lens), S,
-                   block_tables.shape[1] if block_tables.dim() == 2 else 0, int(max_context_len),
-                   int(window))
+    s = PkvSeqs(_ptr(block_tables), _ptr(context_lens), S,
+                block_tables.shape[1] if block_tables.dim() == 2 else 0, int(max_context_len),
+                int(window))
+    s._tensors = (block_tables, context_lens)  # alive as long as the struct that points at them
+    return s
 
 
 def kv_append(cache: PkvCache, seqs: PkvSeqs, k_new, v_new, cu_new_lens, total_new: int,

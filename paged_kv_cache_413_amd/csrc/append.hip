@@ -107,25 +107,32 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
 
 // ---- MXFP4 ----------------------------------------------------------------------------
 // Encoding of one 32-element block (OCP Microscaling conversion, as the cache
-// description states it): the scale byte is max(E - 2, 0), E the bf16 exponent field
-// of the largest magnitude (floor(log2) of a normal value is E - 127; a zero or
-// subnormal maximum takes the clamp, byte 0 = 2^-127); each element's magnitude q =
-// |x| / 2^(byte - 127) -- exact: a power-of-two scaling of a bf16 value, below 8 -- is
-// rounded to nearest on the E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even
-// code, which is a count of the midpoints q passes: strictly for midpoints whose lower
-// neighbour is even (the tie stays there), inclusively for the others; above 5 the
-// count reaches 7 (6.0), which also clamps everything above 6.
+// description states it): one shared power-of-two scale, then every element rounded
+// onto the E2M1 grid 0, .5, 1, 1.5, 2, 3, 4, 6 (mx_encode32).
 struct MxCodes {
   uint32_t w[4];  // nibble e of w[c] = code of element 8c + e
   uint32_t scale;
 };
 
-__device__ __forceinline__ uint32_t e2m1_magnitude(float q) {
-  return uint32_t(q > 0.25f) + uint32_t(q >= 0.75f) + uint32_t(q > 1.25f) + uint32_t(q >= 1.75f) +
-         uint32_t(q > 2.5f) + uint32_t(q >= 3.5f) + uint32_t(q > 5.0f);
+// Two values (low nibble: a) into byte `byte` of `w` as E2M1 codes of value / scale:
+// the hardware conversion rounds to nearest on the E2M1 grid with ties to the even
+// code, clamps magnitudes above 6 to 6, keeps the sign (of zero too) and handles
+// subnormal inputs exactly; it reads only the exponent field of `scale`.
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, float a, float b, float scale, int byte) {
+  switch (byte) {  // the byte select is an immediate
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, scale, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, scale, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, scale, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, scale, 3);
+  }
 }
 
-// 32 consecutive bf16 values at `src` (64-byte aligned).
+// 32 consecutive bf16 values at `src` (64-byte aligned).  The scale byte is max(E - 2,
+// 0), E the bf16 exponent field of the largest magnitude (floor(log2) of a normal value
+// is E - 127; a zero or subnormal maximum takes the clamp, byte 0 = 2^-127); each
+// element is then x / 2^(byte - 127) rounded onto the E2M1 grid (e2m1_pair).  The
+// scale passed to the conversion is the float whose exponent field is the byte (for
+// byte 0 that is +0.0, whose exponent field 0 the conversion reads as 2^-127).
 __device__ __forceinline__ MxCodes mx_encode32(const uint16_t* __restrict__ src) {
   uint32_t h[16];
 #pragma unroll
@@ -142,16 +149,14 @@ __device__ __forceinline__ MxCodes mx_encode32(const uint16_t* __restrict__ src)
   const uint32_t E = amax >> 7;
   MxCodes r;
   r.scale = E >= 2 ? E - 2 : 0;
-  const float inv = __uint_as_float((254u - r.scale) << 23);  // 2^(127 - byte), a normal float
+  const float scale = __uint_as_float(r.scale << 23);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint32_t w = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = 8 * c + e;
-      const uint32_t bits = (h[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-      const float q = __uint_as_float((bits & 0x7fffu) << 16) * inv;
-      w |= (e2m1_magnitude(q) | ((bits >> 12) & 8u)) << (4 * e);
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t bits = h[4 * c + p];  // elements 8c + 2p (low half) and 8c + 2p + 1
+      w = e2m1_pair(w, __uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u), scale, p);
     }
     r.w[c] = w;
   }

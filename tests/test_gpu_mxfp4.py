@@ -145,3 +145,64 @@ def test_mx_window(gpu_lib, name, window):
     assert_lse_close(lse, ref[1], "mxfp4", f"window={window}")
     if wl.num_prefill:
         assert_close(pf, ref[2], "mxfp4", f"window={window} prefill")
+
+
+def _edge_blocks(rng, n):
+    """n blocks of 32 bf16 values (as float32, exactly representable) that reach the
+    encoder's edges: exact midpoints of the E2M1 grid (ties to even), magnitudes above
+    6 X (clamped), zeros and negative zeros, blocks of bf16 subnormals (scale byte 0),
+    subnormals beside a small normal maximum, values near the bf16 maximum (scale
+    byte 252), and plain N(0, 1) values."""
+    out = np.empty((n, 32), np.float32)
+    ties = np.array([6, .25, .75, 1.25, 1.75, 2.5, 3.5, 5, .5, 1, 1.5, 2, 3, 4, 0, 0.125])
+    for i in range(n):
+        kind, k = i % 7, int(rng.integers(-20, 20))
+        if kind == 0:
+            v = rng.permutation(np.concatenate([ties, -ties])) * 2.0 ** k
+        elif kind == 1:
+            v = rng.choice([7.5, 7.0, 6.5, 6.25, 5.5, 0.3, -7.75, 1.0], 32) * 2.0 ** k
+        elif kind == 2:
+            v = np.where(rng.random(32) < .5, -0.0, 0.0)
+        elif kind == 3:
+            v = rng.integers(-127, 128, 32) * 2.0 ** -133
+        elif kind == 4:
+            v = rng.integers(-127, 128, 32) * 2.0 ** -133
+            v[int(rng.integers(32))] = 2.0 ** -124
+        elif kind == 5:
+            v = rng.choice([3.3e38, -3.0e38, 1.7e38, 2.5e37, 1.0], 32)
+        else:
+            v = rng.standard_normal(32)
+        b = (np.asarray(v, np.float32).view(np.uint32) + 0x8000) >> 16   # to bf16 (near), then back
+        out[i] = (b.astype(np.uint32) << 16).view(np.float32)
+    return out
+
+
+def test_mx_append_encodes_edge_values(gpu_lib):
+    """kv_append into an MXFP4 cache, bit for bit against the oracle's codec, on blocks
+    built to hit every rounding, clamping and scale edge of the encoding."""
+    from paged_kv_cache_413_amd import binding as B
+    rng = np.random.default_rng(4130)
+    T, H, D, P = 32, 2, 64, 32
+    print(f"[case] mxfp4 append edges T={T} H={H} D={D}", flush=True)
+    tile = B.paged_kv_page_bytes(B.PKV_MXFP4, P, H, D) // (2 * H)
+    pool = torch.zeros((1, 2, H, tile), dtype=torch.uint8, device="cuda")
+    cache = B.make_cache(pool, P, H, D, B.PKV_MXFP4)
+    table = torch.zeros((1, 1), dtype=torch.int32, device="cuda")       # page 0
+    lens = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    seqs = B.make_seqs(table, lens, T)
+    vals = {kv: _edge_blocks(rng, T * H * D // 32).reshape(T, H, D) for kv in ("k", "v")}
+    dev = {kv: torch.from_numpy(x).to("cuda").to(torch.bfloat16) for kv, x in vals.items()}
+    torch.cuda.synchronize()
+    assert int(table.max()) == 0 and int(lens[0]) == T, "table or lengths changed"
+    B.kv_append(cache, seqs, dev["k"], dev["v"], cu, T)
+    row = D // 2 + D // 32
+    kout = torch.zeros((1, T, H, row), dtype=torch.uint8, device="cuda")
+    vout = torch.zeros_like(kout)
+    B.paged_kv_debug_gather(cache, seqs, kout, vout)
+    torch.cuda.synchronize()
+    for kv, got in (("k", kout), ("v", vout)):
+        codes, scales = oracle.mx_encode(vals[kv].astype(np.float64))
+        g = got[0].cpu().numpy()
+        assert np.array_equal(mx_unpack(g[..., :D // 2]), codes), f"{kv} codes differ"
+        assert np.array_equal(g[..., D // 2:], scales), f"{kv} scales differ"
