@@ -450,7 +450,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       if (tid < MXK) {
         const int tk = tid >> 4, j = (tid & 15) >> 2, cc = tid & 3;
         Frag8 f;
-        f.v = fp4x8_to_bf16(r.kw, e8m0_value(r.ks & 255u));
+        f.v = fp4x8_to_bf16(r.kw, e8m0_operand(r.ks & 255u));
         *reinterpret_cast<uint4*>(dst + j * SL::KCHUNK + tk * 64 + 16 * (cc ^ ((tk >> 1) & 3))) = f.q;
       }
       if (tid < MXV) {
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const int e = 2 * w + k, byte = e * (D / 32) + j;  // scale of position 8cc + e, block j
-            const float sc = e8m0_value((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u);
+            const float sc = e8m0_operand((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u);
             const uint32_t x = fp4_pair_to_bf16(r.vw, sc, w);
             h[k] = tok_of(cc, e) < nvalid ? (k ? (x >> 16) : (x & 0xffffu)) : 0u;  // V past the end: 0
           }
