@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       const auto rv = tile_rsrc(Kt + kv_stride_b, tb);
       const uint32_t codes = uint32_t(P) * (D / 2);
       if (tid < MXK) {
-        const int tk = tid >> 4, j = (tid & 15) >> 2, cc = tid & 3;
+        const int tk = tid / (D / 8), j = (tid % (D / 8)) >> 2, cc = tid & 3;  // token, block, 8-dim group
         const uint32_t row = slot0 + uint32_t(tk);
         r.kw = __builtin_amdgcn_raw_buffer_load_b32(rk, row * (D / 2) + 4 * (cc * (D / 32) + j), 0, 0);
         r.ks = __builtin_amdgcn_raw_buffer_load_b8(rk, codes + row * (D / 32) + j, 0, 0);
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       char* dst = smem + stage * SL::BYTES;
       const int nvalid = L - (blk << LOG2_BT);
       if (tid < MXK) {
-        const int tk = tid >> 4, j = (tid & 15) >> 2, cc = tid & 3;
+        const int tk = tid / (D / 8), j = (tid % (D / 8)) >> 2, cc = tid & 3;  // token, block, 8-dim group
         Frag8 f;
         f.v = fp4x8_to_bf16(r.kw, e8m0_operand(r.ks & 255u));
         *reinterpret_cast<uint4*>(dst + j * SL::KCHUNK + tk * 64 + 16 * (cc ^ ((tk >> 1) & 3))) = f.q;
