@@ -246,6 +246,7 @@ struct PrefillPlan {
   // once -- instead of the query-tiled prefill kernels.
   bool via_decode;
   DecodePlan dec;
+  int per_wave;  // chunks the per-wave prefill kernel runs (see mfma_prefill_geometry)
 };
 
 PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q_heads,
@@ -263,7 +264,7 @@ PrefillPlan plan_prefill(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num
     }
   }
   int qw = 1, resident_items = 1;
-  pkv::mfma_prefill_geometry(c.dtype, c.head_dim, G, c.page_size, &qw, &resident_items);
+  pkv::mfma_prefill_geometry(c.dtype, c.head_dim, G, c.page_size, max_q_len, &qw, &resident_items, &p.per_wave);
   p.qtiles = int(cdiv(max_q_len, qw));
   const int64_t base = int64_t(s.num_seqs) * c.num_kv_heads * p.qtiles;
   const int64_t resident = std::max(1, resident_items);
@@ -456,6 +457,7 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
     char* ws = static_cast<char*>(workspace);
     a.max_splits = p.splits;
     a.pf_qtiles = p.qtiles;
+    a.pf_per_wave = p.per_wave;
     a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
     a.ws_o = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
     return launch_status(pkv::launch_mfma_prefill(a, hs), "paged_attn_prefill_chunk");

@@ -49,8 +49,10 @@ struct AttnArgs {
   // per-wave descriptor of its first (sequence, kv head) segment
   int num_waves, min_share;
   int4* ws_desc;
-  // matrix-core prefill: query tiles per (sequence, kv head) (key splits: max_splits)
+  // matrix-core prefill: query tiles per (sequence, kv head) (key splits: max_splits),
+  // and whether the per-wave kernel runs them (else the LDS-shared one)
   int pf_qtiles;
+  int pf_per_wave;
 };
 
 // Occupancy-derived number of workgroups of `block` threads of `kernel` that fit on
@@ -77,8 +79,8 @@ hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t 
 // Matrix-core prefill kernels (prefill_mfma.hip): same support as the decode kernels.
 // Queries of one (sequence, kv head) per work item and work items resident at once,
 // for the prefill kernel these arguments select.
-void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
-                           int* resident_items);
+void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int max_q_len,
+                           int* queries_per_item, int* resident_items, int* per_wave);
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t stream);
 
 // Debug gather

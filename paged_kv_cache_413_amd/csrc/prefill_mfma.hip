@@ -609,7 +609,7 @@ template <int KV, int D, int G, bool SMALLP>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int groups = a.seqs.num_seqs * a.cache.num_kv_heads * a.max_splits;
   const int64_t grid = int64_t((groups + kXcds - 1) / kXcds) * kXcds * a.pf_qtiles;
-  if constexpr (SMALLP) {  // one wave per item (pages of fewer than 32 tokens)
+  if (SMALLP || a.pf_per_wave) {  // one wave per item (pages of fewer than 32 tokens, short chunks)
     hipLaunchKernelGGL((prefill_kernel<KV, D, G, SMALLP>), dim3(unsigned(grid)), dim3(64), 0, st, a);
   } else {
     hipLaunchKernelGGL((prefill_lds_kernel<KV, D, G>), dim3(unsigned(grid)), dim3(64 * kPfWaves), 0, st, a);
@@ -650,20 +650,32 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int* queries_per_item,
-                           int* resident_items) {
-  const bool lds = page_size >= BT;
-  *queries_per_item = (16 / group) * (lds ? kPfTiles * kPfWaves : head_dim == 128 ? kPrefillTiles<128> : kPrefillTiles<64>);
+// Chunks that one wave's tiles cover whole (up to kPrefillTiles x 16/G queries, e.g. 8
+// tokens verified per sequence at G = 4, D = 128) run on the per-wave kernel: a
+// workgroup of the LDS-shared kernel covers kPfTiles x kPfWaves x 16/G queries (64 at
+// G = 4), so on such chunks 7/8 of its rows would be empty while it still stages every
+// block; one wave per (sequence, kv head, key split) streams each block once instead.
+void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int max_q_len,
+                           int* queries_per_item, int* resident_items, int* per_wave) {
+  const int wave_queries = (16 / group) * (head_dim == 128 ? kPrefillTiles<128> : kPrefillTiles<64>);
+  const bool pw = page_size < BT || max_q_len <= wave_queries;
+  *per_wave = pw;
+  *queries_per_item = pw ? wave_queries : (16 / group) * kPfTiles * kPfWaves;
   const void* k;
-  if (kv_dtype == DT_MXFP4) {
-    k = head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 64, 4>)
-                       : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 128, 4>);
-  } else if (lds) {
-    k = kv_dtype == DT_BF16
-            ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 64, 4>)
-                              : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 128, 4>))
-            : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 64, 4>)
-                              : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 128, 4>));
+  if (!pw) {
+    k = kv_dtype == DT_BF16 ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 64, 4>)
+                                              : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_BF16, 128, 4>))
+        : kv_dtype == DT_FP8 ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 64, 4>)
+                                               : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_FP8, 128, 4>))
+                             : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 64, 4>)
+                                               : reinterpret_cast<const void*>(&prefill_lds_kernel<DT_MXFP4, 128, 4>));
+  } else if (page_size >= BT) {
+    k = kv_dtype == DT_BF16 ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 64, 4, false>)
+                                              : reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 128, 4, false>))
+        : kv_dtype == DT_FP8 ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 64, 4, false>)
+                                               : reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 128, 4, false>))
+                             : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 64, 4, false>)
+                                               : reinterpret_cast<const void*>(&prefill_kernel<DT_MXFP4, 128, 4, false>));
   } else {
     k = kv_dtype == DT_BF16
             ? (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_BF16, 64, 4, true>)
@@ -671,7 +683,7 @@ void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size,
             : (head_dim == 64 ? reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 64, 4, true>)
                               : reinterpret_cast<const void*>(&prefill_kernel<DT_FP8, 128, 4, true>));
   }
-  *resident_items = resident_blocks(k, lds ? 64 * kPfWaves : 64);
+  *resident_items = resident_blocks(k, pw ? 64 : 64 * kPfWaves);
 }
 
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t st) {

@@ -30,6 +30,9 @@ CASES = {
     # G = 8, pages of 32; and at D = 128, G = 16, pages of 128 with a first chunk
     "pf64": (3, dict(num_seqs=5, num_prefill=2, prefill_chunk=[40, 75], prefill_cached=[33, 100], median=50,
                      clip=(1, 200), kv_dtype="mxfp4", head_dim=64, num_q_heads=16, num_kv_heads=2, page_size=32)),
+    # chunks of 5..8 queries at G = 4: the per-wave prefill kernel on pages of 64
+    "mid": (3, dict(num_seqs=3, num_prefill=3, prefill_chunk=[8, 6, 5], prefill_cached=[300, 64, 1000],
+                    median=60, clip=(1, 300), kv_dtype="mxfp4")),
     "pf_g16": (3, dict(num_seqs=4, num_prefill=2, prefill_chunk=[64, 23], prefill_cached=[0, 250], median=60,
                        clip=(1, 300), kv_dtype="mxfp4", num_q_heads=32, num_kv_heads=2, page_size=128)),
 }

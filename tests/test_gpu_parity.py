@@ -342,6 +342,11 @@ PREFILL_EDGES = [
     (16, [25, 50], [7, 100], 64, 8, 128),                     # G = 8, pages of 16
     (8, [20, 3], [13, 60], 32, 2, 64),                        # G = 16, pages of 8
     (64, [300, 5], [600, 2000], 32, 8, 128),                  # several query waves
+    # chunks one wave covers (at most 2 tiles x 16/G queries for D = 128, 4 tiles for
+    # D = 64) run on the per-wave kernel with pages of >= 32 too
+    (64, [5, 8, 7, 6], [100, 700, 2000, 64], 32, 8, 128),     # G = 4: 8 verified tokens
+    (128, [20, 32, 9], [0, 257, 1000], 16, 16, 128),          # G = 1: up to 32 queries
+    (32, [12, 16], [33, 400], 16, 4, 64),                     # G = 4, D = 64: up to 16
 ]
 
 
@@ -537,6 +542,7 @@ FP8_PREFILL = [
     (16, [40, 9], [31, 300], 64, 8, 128, 0),           # per-wave kernel (pages of 16), G = 8
     (64, [4, 3, 1], [500, 64, 2000], 32, 8, 128, 0),   # short chunks: decode kernels
     (128, [100, 33], [0, 700], 16, 8, 64, 90),         # D = 64, G = 2, window
+    (64, [8, 6, 5], [300, 1000, 40], 32, 8, 128, 0),   # per-wave kernel, pages of 64
 ]
 
 
