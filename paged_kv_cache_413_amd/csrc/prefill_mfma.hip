@@ -650,15 +650,18 @@ hipError_t dispatch_d(const AttnArgs& a, hipStream_t st) {
 
 }  // namespace
 
-// Chunks that one wave's tiles cover whole (up to kPrefillTiles x 16/G queries, e.g. 8
-// tokens verified per sequence at G = 4, D = 128) run on the per-wave kernel: a
+// Chunks that at most two waves' tiles cover (up to 2 x kPrefillTiles x 16/G queries,
+// e.g. 16 tokens verified per sequence at G = 4, D = 128) run on the per-wave kernel: a
 // workgroup of the LDS-shared kernel covers kPfTiles x kPfWaves x 16/G queries (64 at
-// G = 4), so on such chunks 7/8 of its rows would be empty while it still stages every
-// block; one wave per (sequence, kv head, key split) streams each block once instead.
+// G = 4), so on such chunks most of its rows would be empty while it still stages every
+// block; one or two waves per (sequence, kv head, key split), on one XCD, stream each
+// block instead (the second from L2).  Measured on the Llama-shaped batch, 64 sequences:
+// 8 tokens 122 us (LDS-shared 284), 16 tokens 158 us (290); from 32 tokens the
+// LDS-shared kernel is as fast or faster (32: 296 against 303 us; 64: 307 against 510).
 void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size, int max_q_len,
                            int* queries_per_item, int* resident_items, int* per_wave) {
   const int wave_queries = (16 / group) * (head_dim == 128 ? kPrefillTiles<128> : kPrefillTiles<64>);
-  const bool pw = page_size < BT || max_q_len <= wave_queries;
+  const bool pw = page_size < BT || max_q_len <= 2 * wave_queries;
   *per_wave = pw;
   *queries_per_item = pw ? wave_queries : (16 / group) * kPfTiles * kPfWaves;
   const void* k;

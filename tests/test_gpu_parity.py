@@ -345,6 +345,7 @@ PREFILL_EDGES = [
     # chunks one wave covers (at most 2 tiles x 16/G queries for D = 128, 4 tiles for
     # D = 64) run on the per-wave kernel with pages of >= 32 too
     (64, [5, 8, 7, 6], [100, 700, 2000, 64], 32, 8, 128),     # G = 4: 8 verified tokens
+    (64, [16, 12, 9], [300, 1000, 40], 32, 8, 128),           # G = 4: two query tiles
     (128, [20, 32, 9], [0, 257, 1000], 16, 16, 128),          # G = 1: up to 32 queries
     (32, [12, 16], [33, 400], 16, 4, 64),                     # G = 4, D = 64: up to 16
 ]
