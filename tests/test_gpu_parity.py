@@ -426,6 +426,8 @@ WINDOWS = [
     (3, dict(num_seqs=0, num_prefill=5, prefill_chunk=[4, 1, 3, 4, 2],
              prefill_cached=[300, 40, 900, 64, 1000]), 33),                        # short chunks, decode kernels
     (3, dict(num_seqs=2, num_prefill=2, prefill_chunk=[40, 9], prefill_cached=[31, 300], page_size=16), 25),
+    (3, dict(num_seqs=2, num_prefill=3, prefill_chunk=[16, 7, 12], prefill_cached=[500, 90, 1200]), 60),
+    # ^ chunks of 5..16 queries on pages of 64: the per-wave prefill kernel
 ]
 
 
