@@ -512,6 +512,8 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     const int blk2 = min(b0 + i + 2, last);
     stash_any(rs, (i + 2) % kPfStages, blk2);
     fetch_any(rs, min(b0 + i + 4, last));
+    // a wave whose rows all lie past the chunk (short chunks) only stages its share
+    if (live) {
     if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
       for (int r = 0; r < NT; ++r)
@@ -542,6 +544,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       __builtin_amdgcn_sched_group_barrier(0x0002, PKV_PF_SCHED, 0);  // vector ALU
     }
 #endif
+    }
     stage_barrier();
   };
   if (nblk > 0) {
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     stash_any(rb, 1, min(b0 + 1, last));
     fetch_any(rb, min(b0 + 3, last));
     stage_barrier();
-    scores(0, sa_);
+    if (live) scores(0, sa_);
   }
   int i = 0;
   for (; i + 1 < nblk; i += 2) {
