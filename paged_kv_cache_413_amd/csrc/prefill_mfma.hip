@@ -458,15 +458,18 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
         Frag8 f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {  // positions 8cc + 2w, +1: each code with its own scale
-          uint32_t h[2];
+          uint32_t x[2];
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
-            const int e = 2 * w + k, byte = e * (D / 32) + j;  // scale of position 8cc + e, block j
-            const float sc = e8m0_operand((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u);
-            const uint32_t x = fp4_pair_to_bf16(r.vw, sc, w);
-            h[k] = tok_of(cc, e) < nvalid ? (k ? (x >> 16) : (x & 0xffffu)) : 0u;  // V past the end: 0
+            const int byte = (2 * w + k) * (D / 32) + j;  // scale of position 8cc + 2w + k, block j
+            x[k] = fp4_pair_to_bf16(r.vw, e8m0_operand((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u), w);
           }
-          f.w[w] = h[0] | (h[1] << 16);
+          f.w[w] = (x[0] & 0xffffu) | (x[1] & 0xffff0000u);  // low half of the first, high of the second
+        }
+        if (nvalid < BT) {  // wave-uniform: the sequence's last, partial block; V past its end: 0
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            f.w[w] &= (tok_of(cc, 2 * w) < nvalid ? 0x0000ffffu : 0u) | (tok_of(cc, 2 * w + 1) < nvalid ? 0xffff0000u : 0u);
         }
         *reinterpret_cast<uint4*>(dst + SL::KBYTES + d * 64 + 16 * (cc ^ ((d >> 1) & 3))) = f.q;
       }
