@@ -499,25 +499,28 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   };
   // Step i: block i+2 goes from its register slot into stage (i+2)%3 -- last read (V
   // of block i-1) before the previous step's barrier -- and the slot refills with block
-  // i+4 (clamped to the last block: a harmless repeat near the end).  Then block i is
-  // folded: its scores (cur, from the previous step) are masked where the block
-  // reaches a row's position or lies past the wave's rows (every weight there is 0,
-  // so such a block changes nothing), maxima and the rare rescale vote come first, and
-  // the main region -- exponentials of block i, the scores of block i+1 into nxt
-  // (stage (i+1)%3, complete since the previous barrier; clamped at the end), the
-  // P.V products of block i -- is one straight-line stretch in which the scheduler
-  // interleaves the matrix-core and vector instructions.  With bf16 and FP8 caches the
-  // scores of block i+1 are issued first instead, so that their matrix instructions run
-  // under the dependent chain of row maxima (measured on the mixed batch: prefill
-  // 171-172 -> 166.5 us with bf16, unchanged with FP8); with MXFP4, whose staging
-  // conversions already sit at the top of the step, that order was slower (226 -> 242 us).
-  constexpr bool kEarlyScores = KV != DT_MXFP4;
+  // i+4 (clamped to the last block: a harmless repeat near the end).  The scores of
+  // block i+1 go into nxt (stage (i+1)%3, complete since the previous barrier; clamped
+  // at the end).  Then block i is folded: its scores (cur, from the previous step) are
+  // masked where the block reaches a row's position or lies past the wave's rows
+  // (every weight there is 0, so such a block changes nothing), maxima and the rare
+  // rescale vote come first, then the exponentials and P.V products of block i, which
+  // the scheduler interleaves.  Where the scores of block i+1 are issued decides what
+  // their matrix instructions overlap (measured on the mixed batch, prefill call):
+  // with bf16 and FP8 caches after the staging, under the dependent chain of row
+  // maxima (bf16 171-172 -> 166.5 us against issuing them with the exponentials, FP8
+  // unchanged); with MXFP4 before the staging, under its decoding conversions
+  // (226.9 -> 208.6 us).  Each cache measured slower with the other's order (bf16
+  // 174 us, MXFP4 242 us).
+  constexpr bool kFirst = KV == DT_MXFP4;          // scores(i+1) before the staging
+  constexpr bool kEarlyScores = KV != DT_MXFP4;    // scores(i+1) after it, before the maxima
   const int last = b1 - 1;
   std::conditional_t<KV == DT_MXFP4, MxSlot<MXS>, uint4[SL::PER_WAVE]> ra, rb;
   float sa_[NT][8], sb_[NT][8];
   auto step = [&](auto& rs, int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
     const int t = (b0 + i) << LOG2_BT;
     const int blk2 = min(b0 + i + 2, last);
+    if constexpr (kFirst) { if (live) scores(min(i + 1, nblk - 1), nxt); }
     stash_any(rs, (i + 2) % kPfStages, blk2);
     fetch_any(rs, min(b0 + i + 4, last));
     // a wave whose rows all lie past the chunk (short chunks) only stages its share
@@ -540,7 +543,6 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     for (int dt = 0; dt < D / 16; ++dt) vv[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
     Frag8 pa[NT];
     softmax_tail<NT>(st, cur, qk_scale, off, pa);
-    if constexpr (!kEarlyScores) scores(min(i + 1, nblk - 1), nxt);
 #pragma unroll
     for (int r = 0; r < NT; ++r)
 #pragma unroll
