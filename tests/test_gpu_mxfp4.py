@@ -19,7 +19,7 @@ CASES = {
     # D=64, G=8, pages of 32
     "dec64": (2, dict(num_seqs=5, len_range=(1, 400), kv_dtype="mxfp4", head_dim=64, num_q_heads=16,
                       num_kv_heads=2, page_size=32)),
-    # two 70-token prefill chunks (the per-wave prefill kernel) and 7 decode sequences
+    # two 70-token prefill chunks (the LDS-shared prefill kernel) and 7 decode sequences
     "mixed": (3, dict(num_seqs=7, num_prefill=2, prefill_chunk=70, prefill_cached=190, median=60,
                       clip=(1, 400), kv_dtype="mxfp4")),
     # chunks of 1, 3 and 4 tokens (at most 16 / G: the balanced decode kernels), odd and

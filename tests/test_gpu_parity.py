@@ -342,8 +342,8 @@ PREFILL_EDGES = [
     (16, [25, 50], [7, 100], 64, 8, 128),                     # G = 8, pages of 16
     (8, [20, 3], [13, 60], 32, 2, 64),                        # G = 16, pages of 8
     (64, [300, 5], [600, 2000], 32, 8, 128),                  # several query waves
-    # chunks one wave covers (at most 2 tiles x 16/G queries for D = 128, 4 tiles for
-    # D = 64) run on the per-wave kernel with pages of >= 32 too
+    # chunks of at most two waves' queries (a wave holds 2 tiles x 16/G queries for
+    # D = 128, 4 tiles for D = 64) run on the per-wave kernel with pages of >= 32 too
     (64, [5, 8, 7, 6], [100, 700, 2000, 64], 32, 8, 128),     # G = 4: 8 verified tokens
     (64, [16, 12, 9], [300, 1000, 40], 32, 8, 128),           # G = 4: two query tiles
     (128, [20, 32, 9], [0, 257, 1000], 16, 16, 128),          # G = 1: up to 32 queries
