@@ -277,7 +277,7 @@ def main():
 
     import workloads
     from paged_kv_cache_413_amd import binding
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_mb > 0:

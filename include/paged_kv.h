@@ -27,9 +27,14 @@
  *   - Values the host cannot see (page ids inside a block table, device-side
  *     lengths) must satisfy the stated contract; a violation is undefined
  *     behaviour (typically a memory fault), exactly as an out-of-range index into
- *     any device array.
+ *     any device array -- unless PKV_DEBUG=1 is set in the environment: then every
+ *     call first validates them on the device (reading only the block tables,
+ *     lengths and prefix sums, or the page pairs of a copy), and a call that breaks
+ *     the contract touches neither the pool nor its outputs and raises bits that
+ *     paged_kv_debug_status() reports.  The variable is read at every call.
  *   - Calls are reentrant: the library keeps no state but cached device
- *     properties and a thread-local error string.
+ *     properties, a thread-local error string, a thread-local test override
+ *     (paged_kv_debug_set_auto_waves) and, per device, the validation flag words.
  */
 #ifndef PAGED_KV_H
 #define PAGED_KV_H
@@ -245,14 +250,58 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
                              size_t workspace_bytes, void* stream);
 
 /* paged_kv_debug_gather -- copy every cached token back into logical order, for
- * checking page addressing bit for bit.  Uses the same page-address code as the
- * attention kernels.
+ * checking the pool's contents bit for bit.  Uses the page-slot addressing of
+ * kv_append (and of the vector-ALU attention kernels); the matrix-core kernels'
+ * own loaders are checked by paged_kv_debug_gather_operands.
  *   k_out, v_out: [num_seqs][max_context_len][num_kv_heads][head_dim] of
  *         cache_dtype; rows t >= context_lens[s] are left untouched.  For MXFP4 a
  *         row is head_dim / 2 bytes of codes in dim order (two per byte, the lower
  *         dim in the low nibble) then its head_dim / 32 scale bytes. */
 int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void* k_out,
                           void* v_out, void* stream);
+
+/* paged_kv_debug_gather_operands -- run the matrix-core attention kernels' own page
+ * loaders over every cached token and write the K and V operands they produce back in
+ * logical order, for checking the hot path's page-gather indexing bit for bit
+ * ([Deep dive] §9, the logical-block -> physical-block figure).
+ *   path: 0 = the decode loaders (a 32-token block straight from the pool into
+ *         operand registers, page ids from a register window of the table; pages of
+ *         8 or 16 tokens look each token's page up); 1 = the prefill loaders (a block
+ *         fetched by a whole workgroup, decoded and staged in LDS, then read back with
+ *         the operand lane map; pages of >= 32 tokens).
+ *   k_out, v_out: [num_seqs][max_context_len][num_kv_heads][head_dim] bfloat16: the
+ *         values the products use -- bf16 caches as stored, FP8 codes widened exactly
+ *         (the per-head scale is applied to the products, not to the operands), MXFP4
+ *         elements times their block scale (exact).  Rows t >= context_lens[s] are
+ *         left untouched.
+ * Caches: BF16 or FP8 with pages of >= 8 tokens (path 1: >= 32), MXFP4 (pages >= 32);
+ * PKV_EUNSUPPORTED otherwise. */
+int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* seqs, int32_t path,
+                                   void* k_out, void* v_out, void* stream);
+
+/* Contract violations found by device validation (PKV_DEBUG=1), as bits. */
+typedef enum {
+  PKV_DEBUG_PAGE_RANGE = 1,  /* a page id the call addresses is outside [0, num_pages) */
+  PKV_DEBUG_LENGTH = 2,      /* a length outside [1, max_context_len], n_s > L_s, or a
+                                prefill chunk longer than L_s or max_q_len */
+  PKV_DEBUG_CU = 4,          /* prefix sums not starting at 0, decreasing, or not ending
+                                at total_new / total_q */
+  PKV_DEBUG_DUP_SLOT = 8,    /* two appended rows name the same (page, slot) */
+  PKV_DEBUG_COPY_PAIRS = 16  /* a copy destination that is also a source, or repeated */
+} pkv_debug_flag_t;
+
+/* The pkv_debug_flag_t bits raised by validated calls on the current device since the
+ * last clear (0 = none), then cleared if `clear` is nonzero; negative pkv_status_t on
+ * error.  Waits for the whole device to finish its work (a debugging call, not for
+ * a hot loop).  Validated calls share the device's flag words: validated calls on
+ * several streams at once race on them. */
+int32_t paged_kv_debug_status(int32_t clear);
+
+/* Test-only: make the balanced decode schedule use `waves` waves instead of the
+ * device's resident count (0 restores it), for the calls of the calling thread --
+ * few waves give long shares and many cut segments on small batches.  The workspace
+ * size query and the call must see the same setting. */
+int paged_kv_debug_set_auto_waves(int32_t waves);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* paged_kv_last_error(void);

@@ -27,7 +27,11 @@ DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
 EXPORTS = ("paged_kv_page_bytes", "kv_append", "kv_copy_pages", "paged_attn_decode_workspace_size",
            "paged_attn_decode", "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
-           "paged_kv_debug_gather", "paged_kv_last_error")
+           "paged_kv_debug_gather", "paged_kv_debug_gather_operands", "paged_kv_debug_status",
+           "paged_kv_debug_set_auto_waves", "paged_kv_last_error")
+
+# device-validation bits (PKV_DEBUG=1), as paged_kv_debug_status reports them
+PKV_DEBUG_PAGE_RANGE, PKV_DEBUG_LENGTH, PKV_DEBUG_CU, PKV_DEBUG_DUP_SLOT, PKV_DEBUG_COPY_PAIRS = 1, 2, 4, 8, 16
 
 
 class PkvCache(ctypes.Structure):
@@ -81,6 +85,12 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_prefill_chunk.restype = c_int32
     lib.paged_kv_debug_gather.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_void_p, c_void_p]
     lib.paged_kv_debug_gather.restype = c_int32
+    lib.paged_kv_debug_gather_operands.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_void_p, c_void_p, c_void_p]
+    lib.paged_kv_debug_gather_operands.restype = c_int32
+    lib.paged_kv_debug_status.argtypes = [c_int32]
+    lib.paged_kv_debug_status.restype = c_int32
+    lib.paged_kv_debug_set_auto_waves.argtypes = [c_int32]
+    lib.paged_kv_debug_set_auto_waves.restype = c_int32
     lib.paged_kv_last_error.argtypes = []
     lib.paged_kv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -192,6 +202,22 @@ def paged_attn_prefill_chunk(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, cu
 def paged_kv_debug_gather(cache: PkvCache, seqs: PkvSeqs, k_out, v_out, stream=None):
     _check(load().paged_kv_debug_gather(ctypes.byref(cache), ctypes.byref(seqs), _ptr(k_out),
                                         _ptr(v_out), _stream(stream)))
+
+
+def paged_kv_debug_gather_operands(cache: PkvCache, seqs: PkvSeqs, path: int, k_out, v_out, stream=None):
+    _check(load().paged_kv_debug_gather_operands(ctypes.byref(cache), ctypes.byref(seqs), int(path),
+                                                 _ptr(k_out), _ptr(v_out), _stream(stream)))
+
+
+def paged_kv_debug_status(clear: bool = True) -> int:
+    r = int(load().paged_kv_debug_status(int(bool(clear))))
+    if r < 0:
+        _check(r)
+    return r
+
+
+def paged_kv_debug_set_auto_waves(waves: int):
+    _check(load().paged_kv_debug_set_auto_waves(int(waves)))
 
 
 def paged_kv_last_error() -> str:

@@ -114,6 +114,7 @@ int check_cache(const pkv_cache_t* c, pkv::CacheArgs& out) {
   out.v_scale = c->v_scale;
   out.k_inv_scale = c->k_inv_scale;
   out.v_inv_scale = c->v_inv_scale;
+  out.debug_flag = nullptr;
   return PKV_OK;
 }
 
@@ -162,16 +163,29 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 constexpr int kMinShareBlocks = 4;  // auto schedule: at least 4 x 32 tokens per wave
 
-// Waves of the balanced schedule: the device's resident count, or PKV_AUTO_WAVES=N
-// (1 <= N <= 65536; for tests and tuning: few waves give long shares and many cut
-// segments on small batches).  Read on every plan, so the size query and the call must
-// see the same value.
+// Test-only override of the balanced schedule's wave count (paged_kv_debug_set_auto_waves;
+// 0 = the device's resident count).  Thread-local, like the error string: it changes only
+// the calls the setting thread makes, and nothing but that explicit call sets it.
+thread_local int g_auto_waves_override = 0;
+
+// Waves of the balanced schedule: the device's resident count, or the test override.
 int auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
-  if (const char* e = std::getenv("PKV_AUTO_WAVES")) {
-    const long n = std::strtol(e, nullptr, 10);
-    if (n >= 1 && n <= (1L << 16)) return int(n);
-  }
+  if (g_auto_waves_override > 0) return g_auto_waves_override;
   return std::max(1, pkv::mfma_auto_waves(kv_dtype, head_dim, group, page_size));
+}
+
+// Device validation of a call before its kernels, when PKV_DEBUG=1 is set in the
+// environment (read at every call; validation adds one small launch per call).
+bool debug_mode() {
+  const char* e = std::getenv("PKV_DEBUG");
+  return e && e[0] && !(e[0] == '0' && e[1] == 0);
+}
+
+int validate(pkv::CacheArgs& c, const pkv::SeqArgs& s, const pkv::ValidateArgs& v, hipStream_t st) {
+  if (!debug_mode()) return PKV_OK;
+  const hipError_t e = pkv::launch_validate(c, s, v, st);
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "device validation: launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
 }
 
 // Partition plan of one decode call.
@@ -329,8 +343,10 @@ int kv_append(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* k_ne
   if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
   if ((st = check_fp8_scales(c, true)) != PKV_OK) return st;
   const int in_dtype = c.dtype == PKV_F32 ? PKV_F32 : PKV_BF16;
-  return launch_status(pkv::launch_kv_append(c, s, k_new, v_new, in_dtype, cu_new_lens, total_new,
-                                             static_cast<hipStream_t>(stream)),
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = validate(c, s, pkv::ValidateArgs{pkv::VK_APPEND, cu_new_lens, total_new, 0, nullptr, nullptr, 0}, hs)) != PKV_OK)
+    return st;
+  return launch_status(pkv::launch_kv_append(c, s, k_new, v_new, in_dtype, cu_new_lens, total_new, hs),
                        "kv_append");
 }
 
@@ -343,8 +359,12 @@ int kv_copy_pages(const pkv_cache_t* cache, const int32_t* src_pages, const int3
   if (num_pairs > 65535) return fail(PKV_EINVAL, "num_pairs must be <= 65535 per call");
   if (num_pairs == 0) return ok();
   if (!src_pages || !dst_pages) return fail(PKV_EINVAL, "src_pages and dst_pages must not be NULL");
-  return launch_status(pkv::launch_copy_pages(c, src_pages, dst_pages, num_pairs, static_cast<hipStream_t>(stream)),
-                       "kv_copy_pages");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  pkv::SeqArgs none{};
+  if ((st = validate(c, none, pkv::ValidateArgs{pkv::VK_COPY, nullptr, 0, 0, src_pages, dst_pages, num_pairs}, hs)) !=
+      PKV_OK)
+    return st;
+  return launch_status(pkv::launch_copy_pages(c, src_pages, dst_pages, num_pairs, hs), "kv_copy_pages");
 }
 
 size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs_t* seqs,
@@ -389,6 +409,9 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
   a.ws_lse = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
   a.ws_o = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_o) : nullptr;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = validate(a.cache, a.seqs, pkv::ValidateArgs{pkv::VK_DECODE, nullptr, 0, 0, nullptr, nullptr, 0}, hs)) !=
+      PKV_OK)
+    return st;
   if (p.mfma) {
     a.num_waves = p.waves;
     a.min_share = kMinShareBlocks;
@@ -443,6 +466,10 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
   a.total_q = total_q;
   a.max_q_len = max_q_len;
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = validate(a.cache, a.seqs,
+                     pkv::ValidateArgs{pkv::VK_PREFILL, cu_q_lens, total_q, max_q_len, nullptr, nullptr, 0}, hs)) !=
+      PKV_OK)
+    return st;
   if (p.via_decode) {
     char* ws = static_cast<char*>(workspace);
     a.ws_lse = reinterpret_cast<float*>(ws + p.dec.off_lse);
@@ -478,8 +505,46 @@ int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void
   if (s.num_seqs > 65535) return fail(PKV_EUNSUPPORTED, "debug gather handles at most 65535 sequences");
   if (!k_out || !v_out) return fail(PKV_EINVAL, "k_out and v_out must not be NULL");
   if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(PKV_EINVAL, "k_out and v_out must be 16-byte aligned");
-  return launch_status(pkv::launch_debug_gather(c, s, k_out, v_out, static_cast<hipStream_t>(stream)),
-                       "paged_kv_debug_gather");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = validate(c, s, pkv::ValidateArgs{pkv::VK_GATHER, nullptr, 0, 0, nullptr, nullptr, 0}, hs)) != PKV_OK)
+    return st;
+  return launch_status(pkv::launch_debug_gather(c, s, k_out, v_out, hs), "paged_kv_debug_gather");
+}
+
+int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* seqs, int32_t path,
+                                   void* k_out, void* v_out, void* stream) {
+  pkv::CacheArgs c;
+  pkv::SeqArgs s;
+  int st;
+  if ((st = check_cache(cache, c)) != PKV_OK) return st;
+  if ((st = check_seqs(seqs, c, s)) != PKV_OK) return st;
+  if (path != 0 && path != 1) return fail(PKV_EINVAL, "path must be 0 (decode loaders) or 1 (prefill loaders)");
+  if (!pkv::operands_supported(c.dtype, c.page_size, c.head_dim, path))
+    return fail(PKV_EUNSUPPORTED, "no matrix-core loader for cache dtype %d, page size %d, path %d", c.dtype,
+                c.page_size, path);
+  if (s.num_seqs == 0) return ok();
+  if (int64_t(s.num_seqs) * c.num_kv_heads > (int64_t(1) << 31) - 1)
+    return fail(PKV_EUNSUPPORTED, "too many (sequence, kv head) pairs");
+  if (!k_out || !v_out) return fail(PKV_EINVAL, "k_out and v_out must not be NULL");
+  if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(PKV_EINVAL, "k_out and v_out must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = validate(c, s, pkv::ValidateArgs{pkv::VK_GATHER, nullptr, 0, 0, nullptr, nullptr, 0}, hs)) != PKV_OK)
+    return st;
+  return launch_status(pkv::launch_debug_operands(c, s, path, k_out, v_out, hs), "paged_kv_debug_gather_operands");
+}
+
+int32_t paged_kv_debug_status(int32_t clear) {
+  int32_t bits = 0;
+  const hipError_t e = pkv::read_debug_status(clear != 0, &bits);
+  if (e != hipSuccess) return fail(PKV_ELAUNCH, "paged_kv_debug_status: %s", hipGetErrorString(e));
+  ok();
+  return bits;
+}
+
+int paged_kv_debug_set_auto_waves(int32_t waves) {
+  if (waves < 0 || waves > (1 << 16)) return fail(PKV_EINVAL, "waves must be in [0, 65536] (got %d)", waves);
+  g_auto_waves_override = waves;
+  return ok();
 }
 
 }  // extern "C"

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
                                                         const void* __restrict__ k_new,
                                                         const void* __restrict__ v_new,
                                                         const int32_t* __restrict__ cu) {
+  if (halted(c)) return;
   const int row = blockIdx.x;
   const int s = owner_of(cu, sq.num_seqs, row);
   const int n = cu[s + 1] - cu[s];
@@ -173,6 +174,7 @@ __global__ __launch_bounds__(64) void kv_append_mx_kernel(CacheArgs c, SeqArgs s
                                                           const uint16_t* __restrict__ k_new,
                                                           const uint16_t* __restrict__ v_new,
                                                           const int32_t* __restrict__ cu) {
+  if (halted(c)) return;
   const int row = blockIdx.x;
   const int s = owner_of(cu, sq.num_seqs, row);
   const int first = cu[s], n = cu[s + 1] - first;
@@ -228,6 +230,7 @@ __global__ __launch_bounds__(64) void kv_append_mx_kernel(CacheArgs c, SeqArgs s
 __global__ __launch_bounds__(256) void debug_gather_mx_kernel(CacheArgs c, SeqArgs sq,
                                                               uint8_t* __restrict__ k_out,
                                                               uint8_t* __restrict__ v_out) {
+  if (halted(c)) return;
   const int s = blockIdx.y;
   const int L = sq.context_lens[s];
   const int D = c.head_dim, H = c.num_kv_heads, P = c.page_size, J = D / 32;
@@ -270,6 +273,7 @@ __global__ __launch_bounds__(256) void debug_gather_mx_kernel(CacheArgs c, SeqAr
 __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs sq,
                                                            uint8_t* __restrict__ k_out,
                                                            uint8_t* __restrict__ v_out) {
+  if (halted(c)) return;
   const int s = blockIdx.y;
   const int L = sq.context_lens[s];
   const int eb = c.dtype == DT_F32 ? 4 : (c.dtype == DT_BF16 ? 2 : 1);
@@ -306,7 +310,9 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(CacheArgs c, SeqArgs 
 // one contiguous range of the pool, so the copy is a plain 16-byte-vector copy;
 // blockIdx.y = pair i, blockIdx.x strides over the page's 16-byte words.
 __global__ __launch_bounds__(256) void copy_pages_kernel(uint4* __restrict__ pool, const int32_t* __restrict__ src,
-                                                          const int32_t* __restrict__ dst, int64_t words) {
+                                                          const int32_t* __restrict__ dst, int64_t words,
+                                                          const int32_t* __restrict__ flag) {
+  if (flag && *flag) return;
   const int i = blockIdx.y;
   const int64_t s = src[i], d = dst[i];
   if (s == d) return;
@@ -323,7 +329,7 @@ hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32
   const int64_t words = int64_t(2) * c.num_kv_heads * tile_bytes(c.dtype, c.page_size, c.head_dim) / 16;
   const int64_t per = std::min<int64_t>(64, (words + 255) / 256);  // workgroups per page
   hipLaunchKernelGGL(copy_pages_kernel, dim3(unsigned(per), unsigned(n)), dim3(256), 0, stream,
-                     static_cast<uint4*>(c.pool), src, dst, words);
+                     static_cast<uint4*>(c.pool), src, dst, words, c.debug_flag);
   return hipGetLastError();
 }
 

@@ -149,6 +149,7 @@ constexpr int kDecodeWavesPerEu = KV == DT_MXFP4 ? PKV_MX_WAVES_PER_EU : PKV_DEC
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<KV>, kDecodeWavesPerEu<KV>))) void decode_fixed_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   const int lane = threadIdx.x & 63;
   const int64_t wid = int64_t(blockIdx.x) * kWgWaves + uniform32(threadIdx.x >> 6);
   const int Hkv = a.cache.num_kv_heads;
@@ -244,6 +245,7 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, const i
 // query per sequence (packed row s) and records of G rows.
 template <int KV, int D, int G, bool SMALLP, bool MQ>
 __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<KV>, kDecodeWavesPerEu<KV>))) void decode_auto_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   constexpr int ROWS = MQ ? 16 : G;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * kWgWaves + uniform32(threadIdx.x >> 6);
@@ -322,6 +324,7 @@ constexpr int kAutoMergeThreads = PKV_AUTO_MERGE_THREADS;
 
 template <int D, int G, bool MQ>
 __global__ __launch_bounds__(kAutoMergeThreads) void merge_auto_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   const int w = blockIdx.x;
   const int4 d = a.ws_desc[w];  // (sequence, kv head, w0, flags)
   if (d.x < 0 || !(d.w & 1)) return;
@@ -337,6 +340,7 @@ __global__ __launch_bounds__(kAutoMergeThreads) void merge_auto_kernel(AttnArgs 
 // Merge of the fixed partitions of one (sequence, kv head).
 template <int D, int G>
 __global__ __launch_bounds__(kMergeThreads) void merge_fixed_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   const int sg = blockIdx.x;
   const int Hkv = a.cache.num_kv_heads;
   const int g = sg % Hkv, s = sg / Hkv;

@@ -103,6 +103,7 @@ __device__ __forceinline__ void combine(float& m, float& l, float* acc, float mo
 
 template <int KV, int QT, int D, int G, bool PREFILL>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   constexpr int LPR = D / 8;        // lanes per token row
   constexpr int RPW = 64 / LPR;     // token rows per wave per step
   const int Hkv = a.cache.num_kv_heads;
@@ -253,6 +254,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 // LSE = log sum_j exp(lse_j), out = sum_j exp(lse_j - LSE) o_j.
 template <int QT, bool PREFILL>
 __global__ __launch_bounds__(128) void merge_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   const int hq = blockIdx.x % a.num_q_heads;
   const int row = blockIdx.x / a.num_q_heads;
   int nkeys;

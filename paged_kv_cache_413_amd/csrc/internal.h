@@ -14,7 +14,15 @@ struct CacheArgs {
   int64_t num_pages;
   int page_size, log2_page, num_kv_heads, head_dim, dtype;
   const float *k_scale, *v_scale, *k_inv_scale, *v_inv_scale;
+  // Device validation (PKV_DEBUG=1): the word the call's validation kernel writes; every
+  // kernel of the call returns at once when it is nonzero.  NULL when not validating.
+  const int32_t* debug_flag;
 };
+
+// True when the call's device validation found a contract violation: the kernel must
+// return before touching the pool or any output (every thread of a workgroup sees the
+// same word, so a workgroup with barriers leaves as a whole).
+__device__ __forceinline__ bool halted(const CacheArgs& c) { return c.debug_flag && *c.debug_flag != 0; }
 
 struct SeqArgs {
   const int32_t* block_tables;
@@ -83,10 +91,33 @@ void mfma_prefill_geometry(int kv_dtype, int head_dim, int group, int page_size,
                            int* queries_per_item, int* resident_items, int* per_wave);
 hipError_t launch_mfma_prefill(const AttnArgs& a, hipStream_t stream);
 
-// Debug gather
+// Device validation of one call (validate.hip), launched before its kernels when
+// PKV_DEBUG=1: page ids the call addresses in [0, num_pages), lengths within their
+// bounds, consistent prefix sums, no two appended rows in one slot, valid copy pairs.
+// On success c.debug_flag points at the word the kernels check.
+enum ValidateKind : int { VK_APPEND = 0, VK_DECODE = 1, VK_PREFILL = 2, VK_GATHER = 3, VK_COPY = 4 };
+struct ValidateArgs {
+  int kind;
+  const int32_t* cu;   // append: cu_new_lens; prefill: cu_q_lens; else NULL
+  int total_rows;      // append: total_new; prefill: total_q
+  int max_q_len;       // prefill
+  const int32_t *src, *dst;  // copy pairs
+  int num_pairs;
+};
+hipError_t launch_validate(CacheArgs& c, const SeqArgs& s, const ValidateArgs& v, hipStream_t stream);
+// Sticky violation bits of the current device since the last clear (synchronizes the device).
+hipError_t read_debug_status(bool clear, int32_t* out);
+
+// Page copy and debug gather
 hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32_t* dst, int n,
                              hipStream_t stream);
 hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,
                                hipStream_t stream);
+
+// The attention kernels' own loaders over every cached token (debug_gather.hip): path 0
+// the decode block pipeline, path 1 the prefill kernel's LDS staging; bf16 operands out.
+bool operands_supported(int kv_dtype, int page_size, int head_dim, int path);
+hipError_t launch_debug_operands(const CacheArgs& c, const SeqArgs& s, int path, void* k_out, void* v_out,
+                                 hipStream_t stream);
 
 }  // namespace pkv

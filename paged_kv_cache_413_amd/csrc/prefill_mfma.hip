@@ -20,7 +20,7 @@
 // merged exactly by a second kernel.  Workgroups go to the XCDs round robin; the
 // grid is ordered so that all query tiles of one (sequence, kv head, split) land on
 // the same XCD and read the same K/V blocks through its L2.
-#include "mfma_common.h"
+#include "stage.h"
 
 namespace pkv {
 namespace {
@@ -91,6 +91,7 @@ __device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D>
 
 template <int KV, int D, int G, bool SMALLP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   constexpr int NT = kPrefillTiles<D>, QPT = PfGeom<G, D>::QPT, QW = PfGeom<G, D>::QW;
   const int lane = threadIdx.x, n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
@@ -182,54 +183,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // block i+1 (matrix cores) while it runs the softmax of block i (vector ALU) and then
 // the P.V products of block i: the two units work at once within each wave, instead
 // of every wave waiting on one then the other between barriers.
-#ifndef PKV_PF_WAVES
-#define PKV_PF_WAVES 8
-#endif
 #ifndef PKV_PF_TILES
 #define PKV_PF_TILES 2
 #endif
-constexpr int kPfWaves = PKV_PF_WAVES;   // waves of a workgroup (a multiple of the 4 SIMDs)
 constexpr int kPfTiles = PKV_PF_TILES;   // 16-row tiles per wave of the LDS-shared kernel
 constexpr int kPfStages = 3;
 #ifndef PKV_PF_SCHED
 #define PKV_PF_SCHED 2  // vector instructions the scheduler puts after each MFMA of a step (0: its own order)
 #endif
-
-template <int KV, int D>
-struct PfStage {
-  // stages hold bf16: FP8 and MXFP4 blocks are decoded once, as they are staged
-  static constexpr int esz = 2;
-  static constexpr int KCHUNK = BT * 32 * esz;   // one 32-dim chunk of the block's K
-  static constexpr int KBYTES = D * BT * esz;
-  static constexpr int BYTES = 2 * KBYTES;       // K and V of one block
-  // fetch geometry of bf16 / FP8 tiles (MXFP4 has its own): 1 KiB pieces of the tile,
-  // one per wave-wide 16-byte load
-  static constexpr int fsz = KV == DT_FP8 ? 1 : 2;
-  static constexpr int FKCHUNK = BT * 32 * fsz;
-  static constexpr int KPIECES = D * BT * fsz / 1024;
-  static constexpr int PIECES = 2 * KPIECES;
-  static constexpr int PER_WAVE = (PIECES + kPfWaves - 1) / kPfWaves;
-  static constexpr bool EVEN = PIECES % kPfWaves == 0;  // else waves >= PIECES copy nothing
-};
-
-// Codes 2w, 2w+1 (byte w) of an E2M1 word times `scale`, as two bf16 (low: code 2w).
-__device__ __forceinline__ uint32_t fp4_pair_to_bf16(uint32_t codes, float scale, int w) {
-  switch (w) {  // the byte select is an immediate
-    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
-    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
-    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
-    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
-  }
-}
-
-// One thread's fetched share of an MXFP4 block (prefill_lds_kernel): a K code word
-// and its scale byte, a V code word and the scale words of its 8 positions (S = 8 for
-// D = 128: one word per position; 4 for D = 64: one word per two positions).
-template <int S>
-struct MxSlot {
-  uint32_t kw, ks, vw;
-  uint32_t vs[S];
-};
 
 // Workgroup barrier; LDS writes and reads of this wave are complete before it.
 __device__ __forceinline__ void stage_barrier() {
@@ -238,20 +199,12 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Eight cache elements of an operand from LDS, as bf16.
-template <int KV>
-__device__ __forceinline__ bf16x8 lds8(const char* p) {
-  Frag8 f;
-  f.q = *reinterpret_cast<const uint4*>(p);  // every stage holds bf16
-  return f.v;
-}
-
 template <int KV, int D, int G>
 __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(kPfWaves / 4, kPfWaves / 4))) void prefill_lds_kernel(AttnArgs a) {
-  using SL = PfStage<KV, D>;
+  if (halted(a.cache)) return;
+  using SL = Stager<KV, D, kPfThreads>;
   constexpr int NT = kPfTiles, QPT = PfGeom<G>::QPT, QWV = NT * QPT;
   constexpr int QWG = kPfWaves * QWV;
-  constexpr int esz = SL::esz;
   __shared__ __attribute__((aligned(1024))) char smem[kPfStages * SL::BYTES];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
@@ -303,196 +256,25 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   for (int r = 0; r < NT; ++r) state_init(st[r]);
 
   const int log2P = a.cache.log2_page, P = 1 << log2P;
-  const int64_t tile_b = tile_bytes(KV, P, D), kv_stride_b = Hkv * tile_b, head_off_b = g * tile_b;
-  const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
-  const char* pool = static_cast<const char*>(a.cache.pool);
-  // this thread's 16-byte share of each of this wave's PER_WAVE pieces of a block
-  // (the page id is a scalar load: it waits on the scalar counter only, never on the
-  // vector loads of the other register slot still in flight)
-  auto fetch = [&](uint4 (&r)[SL::PER_WAVE], int blk) {
-    const int t = blk << LOG2_BT;
-    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-    const int32_t page = ((const_i32_ptr)(uintptr_t)bt)[t >> log2P];
-    const uint32_t slot0 = uint32_t(t & (P - 1));
-    const uint32_t tile_bytes = uint32_t(P) * D * SL::fsz;
-    const char* Kt = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
-    const auto rk = tile_rsrc(Kt, tile_bytes);
-    const auto rv = tile_rsrc(Kt + kv_stride_b, tile_bytes);
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int k = 0; k < SL::PER_WAVE; ++k) {
-      const int p = w + k * kPfWaves;
-      if (!SL::EVEN && p >= SL::PIECES) break;
-      // K or V piece: decided by k alone when the K pieces split evenly over the waves
-      const bool is_k = SL::KPIECES % kPfWaves == 0 ? k * kPfWaves < SL::KPIECES : p < SL::KPIECES;
-      u32x4 v;
-      if (is_k) {
-        const int off = p * 1024;
-        const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t(off / SL::FKCHUNK) * P + slot0) * 32 * SL::fsz +
-                                                           uint32_t(off % SL::FKCHUNK));
-        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * 16, so, 0));
-      } else {
-        const uint32_t so = __builtin_amdgcn_readfirstlane(slot0 * D * SL::fsz + uint32_t(p - SL::KPIECES) * 1024);
-        v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16, so, 0));
-      }
-      r[k] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-  };
-  // bf16 stages are swizzled against LDS bank conflicts: in every 64-byte row (32
-  // tokens of a K chunk or of a V dim), 16-byte segment c of row r is stored at
-  // segment c ^ ((r >> 1) & 3).  A 16-byte-per-lane read is served 8 lanes at a time
-  // from a 128-byte bank window; the operand load's 8 lanes read 8 consecutive rows
-  // (two per window position), and the map spreads them over all of it (measured
-  // conflict-free; the plain layout costs 4 extra cycles per read).  The copy writes
-  // and the operand reads apply the same map.
-  const uint32_t wofs = uint32_t((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 3) & 3)));
-  // Stage a block; in the sequence's last, partial block the V slots past its end are
-  // zeroed here (they may hold anything, NaN included, and a zero weight would not
-  // cancel a NaN), so the operand reads need no tail test.  The lane's 16 bytes are
-  // positions 8(lane & 3) + e of a 32-slot row (bf16) or 16(lane & 1) + e (FP8); the
-  // token at position p of a V row is tok_of(p >> 3, p & 7).
-  auto stash = [&](uint4 (&r)[SL::PER_WAVE], int stage, int blk) {
-    char* dst = smem + stage * SL::BYTES;
-    const int nvalid = L - (blk << LOG2_BT);
-    if (nvalid < BT) {  // wave-uniform, once per sequence
-#pragma unroll
-      for (int k = 0; k < SL::PER_WAVE; ++k) {
-        if (w + k * kPfWaves < SL::KPIECES) continue;
-        uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t keep = 0;
-          if constexpr (SL::fsz == 2) {
-            const int p0 = 8 * (lane & 3) + 2 * j;
-            keep = (tok_of(p0 >> 3, p0 & 7) < nvalid ? 0x0000ffffu : 0u) |
-                   (tok_of((p0 + 1) >> 3, (p0 + 1) & 7) < nvalid ? 0xffff0000u : 0u);
-          } else {
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int pp = 16 * (lane & 1) + 4 * j + b;
-              keep |= tok_of(pp >> 3, pp & 7) < nvalid ? (0xffu << (8 * b)) : 0u;
-            }
-          }
-          wd[j] &= keep;
-        }
-        r[k] = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < SL::PER_WAVE; ++k) {
-      const int p = w + k * kPfWaves;
-      if (!SL::EVEN && p >= SL::PIECES) break;
-      if constexpr (SL::fsz == 2) {
-        *reinterpret_cast<uint4*>(dst + p * 1024 + wofs) = r[k];
-      } else {
-        // an FP8 piece is 32 rows of 32 codes (K: the tokens of one 32-dim chunk; V: 32
-        // dims); the lane's 16 codes (row lane/2, half lane&1) become 32 bytes of bf16,
-        // segments 2(lane&1) and 2(lane&1)+1 of that row of the stage
-        const int row = lane >> 1, s0 = 2 * (lane & 1), swz = (row >> 1) & 3;
-        char* base = dst + (p < SL::KPIECES ? p * SL::KCHUNK : SL::KBYTES + (p - SL::KPIECES) * 32 * 64) + row * 64;
-        const uint32_t wd[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          Frag8 f;
-          f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h], 1.0f, false));
-          f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h], 1.0f, true));
-          f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h + 1], 1.0f, false));
-          f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[2 * h + 1], 1.0f, true));
-          *reinterpret_cast<uint4*>(base + 16 * ((s0 + h) ^ swz)) = f.q;
-        }
-      }
-    }
-  };
-
-  // MXFP4: a thread fetches the codes of 8 dims of one token row of K (one word) with
-  // its scale byte, and of 8 positions of one dim of V (one word) with the scale
-  // words of those positions (one per position: its D/32 block scales); staging
-  // decodes them to the bf16 stage layout above (K: code x block scale; V: each
-  // position with its own scale), so the workgroup decodes every block once and the
-  // waves read bf16 operands.  D = 128: every thread has one K and one V word; D = 64:
-  // the first 256 threads.
-  constexpr int MXK = 32 * D / 8, MXV = 4 * D, MXS = D / 32 >= 4 ? 8 : 4;  // items; scale words of a V item
-  auto fetch_mx = [&](MxSlot<MXS>& r, int blk) {
-    if constexpr (KV == DT_MXFP4) {
-      const int t = blk << LOG2_BT;
-      typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-      const int32_t page = ((const_i32_ptr)(uintptr_t)bt)[t >> log2P];
-      const uint32_t slot0 = uint32_t(t & (P - 1)), tb = uint32_t(tile_b);
-      const char* Kt = pool + int64_t(page) * 2 * kv_stride_b + head_off_b;
-      const auto rk = tile_rsrc(Kt, tb);
-      const auto rv = tile_rsrc(Kt + kv_stride_b, tb);
-      const uint32_t codes = uint32_t(P) * (D / 2);
-      if (tid < MXK) {
-        const int tk = tid / (D / 8), j = (tid % (D / 8)) >> 2, cc = tid & 3;  // token, block, 8-dim group
-        const uint32_t row = slot0 + uint32_t(tk);
-        r.kw = __builtin_amdgcn_raw_buffer_load_b32(rk, row * (D / 2) + 4 * (cc * (D / 32) + j), 0, 0);
-        r.ks = __builtin_amdgcn_raw_buffer_load_b8(rk, codes + row * (D / 32) + j, 0, 0);
-      }
-      if (tid < MXV) {
-        const int d = tid >> 2, cc = tid & 3, m = d & 15, u = d >> 4;
-        const uint32_t sb = slot0 >> 5;
-        r.vw = __builtin_amdgcn_raw_buffer_load_b32(rv, sb * 16 * D + 4 * ((4 * m + cc) * (D / 16) + u), 0, 0);
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const uint32_t so = codes + (sb * 32 + 8 * cc) * (D / 32);  // positions 8cc .. 8cc+7
-#pragma unroll
-        for (int h = 0; h < MXS / 4; ++h) {
-          const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, so + 16 * h, 0, 0));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) r.vs[4 * h + k] = v[k];
-        }
-      }
-    }
-  };
-  auto stash_mx = [&](MxSlot<MXS>& r, int stage, int blk) {
-    if constexpr (KV == DT_MXFP4) {
-      char* dst = smem + stage * SL::BYTES;
-      const int nvalid = L - (blk << LOG2_BT);
-      if (tid < MXK) {
-        const int tk = tid / (D / 8), j = (tid % (D / 8)) >> 2, cc = tid & 3;  // token, block, 8-dim group
-        Frag8 f;
-        f.v = fp4x8_to_bf16(r.kw, e8m0_operand(r.ks & 255u));
-        *reinterpret_cast<uint4*>(dst + j * SL::KCHUNK + tk * 64 + 16 * (cc ^ ((tk >> 1) & 3))) = f.q;
-      }
-      if (tid < MXV) {
-        const int d = tid >> 2, cc = tid & 3, j = d >> 5;
-        Frag8 f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // positions 8cc + 2w, +1: each code with its own scale
-          uint32_t x[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const int byte = (2 * w + k) * (D / 32) + j;  // scale of position 8cc + 2w + k, block j
-            x[k] = fp4_pair_to_bf16(r.vw, e8m0_operand((r.vs[byte >> 2] >> (8 * (byte & 3))) & 255u), w);
-          }
-          f.w[w] = (x[0] & 0xffffu) | (x[1] & 0xffff0000u);  // low half of the first, high of the second
-        }
-        if (nvalid < BT) {  // wave-uniform: the sequence's last, partial block; V past its end: 0
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            f.w[w] &= (tok_of(cc, 2 * w) < nvalid ? 0x0000ffffu : 0u) | (tok_of(cc, 2 * w + 1) < nvalid ? 0xffff0000u : 0u);
-        }
-        *reinterpret_cast<uint4*>(dst + SL::KBYTES + d * 64 + 16 * (cc ^ ((d >> 1) & 3))) = f.q;
-      }
-    }
-  };
-  auto fetch_any = [&](auto& r, int blk) {
-    if constexpr (KV == DT_MXFP4) fetch_mx(r, blk); else fetch(r, blk);
-  };
-  auto stash_any = [&](auto& r, int stage, int blk) {
-    if constexpr (KV == DT_MXFP4) stash_mx(r, stage, blk); else stash(r, stage, blk);
+  const int64_t tile_b = tile_bytes(KV, P, D);
+  const BlockSrc src{static_cast<const char*>(a.cache.pool), a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq,
+                     log2P, Hkv * tile_b, g * tile_b};
+  auto fetch_any = [&](typename SL::Regs& r, int blk) { SL::fetch(r, src, blk, tid); };
+  auto stash_any = [&](typename SL::Regs& r, int stage, int blk) {
+    SL::stash(r, smem + stage * SL::BYTES, L - (blk << LOG2_BT), tid);
   };
 
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
-  const uint32_t lk = uint32_t(n * 64 + 16 * (c ^ ((n >> 1) & 3)));
+  const uint32_t lk = stage_lane_offset(lane);
   // Raw scores of block b0+i (stage i%3) for the wave's tiles.
   auto scores = [&](int i, float (&sc)[NT][8]) {
     const char* stg = smem + (i % kPfStages) * SL::BYTES;
     Block<D> b;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-      b.ka[j] = lds8<KV>(stg + j * SL::KCHUNK + lk);
-      b.kb[j] = lds8<KV>(stg + j * SL::KCHUNK + 16 * 32 * esz + lk);
+      b.ka[j] = SL::k_operand(stg, j, 0, lk);
+      b.kb[j] = SL::k_operand(stg, j, 1, lk);
     }
 #pragma unroll
     for (int r = 0; r < NT; ++r) block_scores<D>(b, qf[r], sc[r]);
@@ -515,7 +297,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   constexpr bool kFirst = KV == DT_MXFP4;          // scores(i+1) before the staging
   constexpr bool kEarlyScores = KV != DT_MXFP4;    // scores(i+1) after it, before the maxima
   const int last = b1 - 1;
-  std::conditional_t<KV == DT_MXFP4, MxSlot<MXS>, uint4[SL::PER_WAVE]> ra, rb;
+  typename SL::Regs ra, rb;
   float sa_[NT][8], sb_[NT][8];
   auto step = [&](auto& rs, int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
     const int t = (b0 + i) << LOG2_BT;
@@ -540,7 +322,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     const char* stg = smem + (i % kPfStages) * SL::BYTES;
     bf16x8 vv[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vv[dt] = lds8<KV>(stg + SL::KBYTES + dt * 16 * 32 * esz + lk);
+    for (int dt = 0; dt < D / 16; ++dt) vv[dt] = SL::v_operand(stg, dt, lk);
     Frag8 pa[NT];
     softmax_tail<NT>(st, cur, qk_scale, off, pa);
 #pragma unroll
@@ -586,6 +368,7 @@ constexpr int kPfMergeThreads = 256;
 
 template <int D, int G>
 __global__ __launch_bounds__(kPfMergeThreads) void prefill_merge_kernel(AttnArgs a) {
+  if (halted(a.cache)) return;
   constexpr int CH = G * D / 4;  // float4 chunks per (row, kv head)
   const int Hkv = a.cache.num_kv_heads, nsplit = a.max_splits;
   const int64_t idx = int64_t(blockIdx.x) * kPfMergeThreads + threadIdx.x;

@@ -1,16 +1,16 @@
 """Cross-request prefix reuse over full pages: a radix tree keyed on token ids.
 
 ("NVIDIA TensorRT-LLM详解：架构、KV Cache、调度与部署实践", §10, cross-request KV reuse:
-filled KV blocks go into a radix search tree, a new request reuses the blocks of its
-longest matching prefix, blocks are evicted by priority (0..100, lowest first) and
-then least recent use, and only requests with the same cache salt share blocks; §11:
-a block that matches only its first tokens is partly reused by copying those tokens
-into a new block, and only leaf blocks are evicted.)
+filled KV blocks go into a radix search tree and a new request reuses the blocks of its
+longest matching prefix; §11: a block that matches only its first tokens is partly
+reused by copying those tokens into a new block of the new request.)
 
 Every node stands for one full page: its key is the page's token ids, its page the
-physical page holding their K/V (layer-independent here: one pool).  Host-side
-bookkeeping only; the device side of a reuse is the block table (shared pages) and
-kv_copy_pages (the partly matched page).
+physical page holding their K/V (one pool).  This is the lookup the kernels' block
+tables need, nothing more: the serving policy around it (eviction order, reference
+counting, tenant isolation) belongs to a scheduler and is not built here.  The device
+side of a reuse is the block table (shared pages) and kv_copy_pages (the partly
+matched page).
 """
 from __future__ import annotations
 
@@ -21,11 +21,7 @@ from dataclasses import dataclass, field
 class _Node:
     key: tuple
     page: int
-    parent: "_Node | None"
     children: dict = field(default_factory=dict)
-    refs: int = 0            # requests holding the page now
-    priority: int = 35
-    tick: int = 0            # last use
 
 
 @dataclass
@@ -35,25 +31,18 @@ class Match:
     partial_tokens: int = 0    # how many (copy-on-partial-reuse copies that page)
 
 
-
 class PrefixIndex:
     def __init__(self, page_size: int):
         assert page_size >= 1
         self.P = page_size
-        self._roots: dict = {}           # salt -> root node
-        self._tick = 0
-        self._by_page: dict = {}         # page -> node
+        self._root = _Node(key=(), page=-1)
+        self._count = 0
 
-    # ---- lookup -------------------------------------------------------------------
-    def match(self, tokens, salt=0, acquire=True) -> Match:
-        """Longest run of full pages of `tokens` in the tree of `salt`, and the best
-        partial match for the page after it.  With acquire, every matched node gains a
-        reference (release() drops it) and counts as just used."""
-        P, node = self.P, self._roots.get(salt)
+    def match(self, tokens) -> Match:
+        """Longest run of full pages of `tokens` in the tree, and the best partial
+        match (fewer than page_size tokens) for the page after it."""
+        P, node = self.P, self._root
         m = Match(pages=[])
-        if node is None:
-            return m
-        self._tick += 1
         i = 0
         while (i + 1) * P <= len(tokens):
             child = node.children.get(tuple(tokens[i * P:(i + 1) * P]))
@@ -61,9 +50,6 @@ class PrefixIndex:
                 break
             node = child
             m.pages.append(child.page)
-            if acquire:
-                child.refs += 1
-                child.tick = self._tick
             i += 1
         rest = tuple(tokens[i * P:(i + 1) * P])
         for key, child in node.children.items():
@@ -74,52 +60,23 @@ class PrefixIndex:
                 m.partial_page, m.partial_tokens = child.page, n
         return m
 
-    # ---- insertion and release --------------------------------------------------------
-    def insert(self, tokens, pages, salt=0, priority=35):
+    def insert(self, tokens, pages):
         """Record the full pages of a sequence (tokens, and the physical page of each of
         its len(tokens) // P full pages).  Pages already in the tree (same prefix) keep
         the tree's page; returns the pages of `pages` the tree did not adopt."""
-        P = self.P
-        node = self._roots.setdefault(salt, _Node(key=(), page=-1, parent=None))
-        self._tick += 1
+        P, node = self.P, self._root
         unused = []
         for i in range(len(tokens) // P):
             key = tuple(tokens[i * P:(i + 1) * P])
             child = node.children.get(key)
             if child is None:
-                child = _Node(key=key, page=int(pages[i]), parent=node, priority=priority, tick=self._tick)
+                child = _Node(key=key, page=int(pages[i]))
                 node.children[key] = child
-                self._by_page[child.page] = child
-            else:
-                if int(pages[i]) != child.page:
-                    unused.append(int(pages[i]))
-                child.priority = max(child.priority, priority)
-                child.tick = self._tick
+                self._count += 1
+            elif int(pages[i]) != child.page:
+                unused.append(int(pages[i]))
             node = child
         return unused
 
-    def release(self, pages):
-        """Drop one reference from each of these tree pages (a request finished)."""
-        for p in pages:
-            node = self._by_page.get(int(p))
-            if node is not None and node.refs > 0:
-                node.refs -= 1
-
-    # ---- eviction -------------------------------------------------------------------
-    def evict(self, count: int):
-        """Remove up to `count` leaves that no request holds -- lowest priority first,
-        then least recently used -- and return their pages (free for reuse).  A parent
-        becomes a leaf, and so a candidate, once its children are gone."""
-        freed = []
-        while len(freed) < count:
-            leaves = [n for n in self._by_page.values() if not n.children and n.refs == 0]
-            if not leaves:
-                break
-            victim = min(leaves, key=lambda n: (n.priority, n.tick))
-            del victim.parent.children[victim.key]
-            del self._by_page[victim.page]
-            freed.append(victim.page)
-        return freed
-
     def __len__(self):
-        return len(self._by_page)
+        return self._count

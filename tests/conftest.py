@@ -21,3 +21,11 @@ def gpu_lib():
     from paged_kv_cache_413_amd import binding
     binding.load()
     return binding
+
+
+@pytest.fixture
+def auto_waves(gpu_lib):
+    """Setter of the balanced decode schedule's wave count for this test (the library's
+    test-only override; 0 = the device's resident count), reset afterwards."""
+    yield gpu_lib.paged_kv_debug_set_auto_waves
+    gpu_lib.paged_kv_debug_set_auto_waves(0)

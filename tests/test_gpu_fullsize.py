@@ -1,10 +1,16 @@
 """Parity at the full sizes of the five workloads, in the launch configuration the
-benchmark times (the workloads' own partition settings), on sampled outputs.
+benchmark times (the workloads' own partition settings), on every output row.
 
-Each workload runs on the GPU whole; the oracle then recomputes, one sequence at a
-time, the shortest and the longest decode sequence plus a few seeded random ones,
-and every query row of the prefill requests, and compares them element by element
-at the same tolerances as the small parity tests."""
+Each workload runs on the GPU whole; the oracle then recomputes every decode sequence
+and every query row of every prefill request, one sequence at a time from a compact
+pool of its own pages (worker processes share the sequences; they never touch the
+GPU), and compares them element by element at the same tolerances as the small parity
+tests.  At full size the balanced decode schedule cuts and merges segments in a pattern
+of its own, so no row is left out."""
+import multiprocessing as mp
+import os
+from concurrent.futures import ProcessPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -15,47 +21,70 @@ from tests.oracle_state import oracle_sequence
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {1: 4, 2: 6, 3: 6, 4: 2, 5: 6, 6: 6}
-
 # (workload, overrides): the six workloads, the Llama batch and the mixed batch with an
 # MXFP4 cache, and the mixed batch with an FP8 cache (the benchmark's other lines)
 CASES = [(c, {}) for c in (1, 2, 3, 4, 5, 6)] + [(2, {"kv_dtype": "mxfp4"}), (3, {"kv_dtype": "mxfp4"}),
                                                  (3, {"kv_dtype": "fp8"})]
 
 
+def _oracle_rows(cfg, over, scales, seqs):
+    """Oracle outputs of sequences `seqs` (run in a worker process, with one BLAS thread:
+    the workers already share the cores)."""
+    from threadpoolctl import threadpool_limits
+    wl = workloads.make(cfg, **over)
+    if scales is not None:
+        wl._scales = scales          # the batch-wide FP8 calibration, computed once by the parent
+    out = {}
+    with threadpool_limits(1):
+        for s in seqs:
+            out[s] = oracle_sequence(wl, s)
+            wl.drop_cache()
+    return out
+
+
+def _workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 @pytest.mark.parametrize("cfg,over", CASES, ids=lambda x: str(x) if isinstance(x, int) else (x.get("kv_dtype") or "-"))
-def test_full_size_sampled_rows(gpu_lib, cfg, over):
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+def test_full_size_every_row(gpu_lib, cfg, over):
     wl = workloads.make(cfg, **over)
     print(f"[case] full-size {wl.name} S={wl.num_seqs} tokens={int(wl.context_lens.sum())}", flush=True)
-    wl.prefetch()
-    db = DeviceBatch(wl)
-    db.fill_history()
-    db.step()
-    torch.cuda.synchronize()
-    dec, dec_lse, pf, pf_lse = db.outputs_f64()
-    del db
-    torch.cuda.empty_cache()
+    scales = wl.fp8_scales() if wl.kv_dtype == "fp8" else None
+    # the longest sequences first, spread over the workers in round-robin batches
+    order = [int(s) for s in np.argsort(-wl.context_lens.astype(np.int64), kind="stable")]
+    nw = _workers()
+    batches = [order[i::nw * 4] for i in range(nw * 4) if order[i::nw * 4]]
+    with ProcessPoolExecutor(nw, mp_context=mp.get_context("spawn")) as ex:
+        futs = [ex.submit(_oracle_rows, cfg, over, scales, b) for b in batches]
+        from tests.device_batch import DeviceBatch
+        wl.prefetch()
+        db = DeviceBatch(wl)
+        db.fill_history()
+        db.step()
+        torch.cuda.synchronize()
+        dec, dec_lse, pf, pf_lse = db.outputs_f64()
+        del db
+        wl.drop_cache()
+        torch.cuda.empty_cache()
+        ref = {}
+        for f in futs:
+            ref.update(f.result())
     npf = wl.num_prefill
-    lens = wl.context_lens[npf:]
-    picks = {npf + int(np.argmin(lens)), npf + int(np.argmax(lens))} if len(lens) else set()
-    rng = np.random.default_rng(cfg)
-    while len(picks) < min(SAMPLES[cfg], wl.num_seqs - npf):
-        picks.add(int(rng.integers(npf, wl.num_seqs)))
-    err = {"decode": 0.0, "prefill": 0.0, "lse": 0.0}
-    for s in sorted(picks):
-        ref_o, ref_l = oracle_sequence(wl, s)
-        r = s - npf
-        err["decode"] = max(err["decode"], assert_close(dec[r:r + 1], ref_o, wl.kv_dtype, f"{wl.name} seq {s}"))
-        err["lse"] = max(err["lse"], assert_lse_close(dec_lse[r:r + 1], ref_l, wl.kv_dtype, f"{wl.name} seq {s}"))
     cu = wl.cu(wl.new_lens)
-    pf_picks = range(npf) if npf <= 8 else sorted(set(np.random.default_rng(cfg + 100).integers(0, npf, 6).tolist()))
-    for s in pf_picks:
-        ref_o, ref_l = oracle_sequence(wl, s)
-        err["prefill"] = max(err["prefill"], assert_close(pf[cu[s]:cu[s + 1]], ref_o, wl.kv_dtype,
-                                                          f"{wl.name} prefill {s}"))
-        err["lse"] = max(err["lse"], assert_lse_close(pf_lse[cu[s]:cu[s + 1]], ref_l, wl.kv_dtype,
-                                                      f"{wl.name} prefill {s}"))
-    print(f"[ok] {wl.name}: {len(picks)} decode sequences, {len(pf_picks)} prefill requests; largest "
-          f"errors ({'abs' if wl.kv_dtype == 'f32' else 'rel'}) decode {err['decode']:.2e}, "
-          f"prefill {err['prefill']:.2e}, lse (abs) {err['lse']:.2e}", flush=True)
+    err = {"decode": 0.0, "prefill": 0.0, "lse": 0.0}
+    for s in range(wl.num_seqs):
+        ref_o, ref_l = ref[s]
+        if s < npf:
+            got_o, got_l, kind = pf[cu[s]:cu[s + 1]], pf_lse[cu[s]:cu[s + 1]], "prefill"
+        else:
+            got_o, got_l, kind = dec[s - npf:s - npf + 1], dec_lse[s - npf:s - npf + 1], "decode"
+        err[kind] = max(err[kind], assert_close(got_o, ref_o, wl.kv_dtype, f"{wl.name} {kind} seq {s}"))
+        err["lse"] = max(err["lse"], assert_lse_close(got_l, ref_l, wl.kv_dtype, f"{wl.name} {kind} seq {s}"))
+    print(f"[ok] {wl.name}: all {wl.num_seqs - npf} decode sequences and {int(cu[npf])} prefill rows of "
+          f"{npf} requests; largest errors ({'abs' if wl.kv_dtype == 'f32' else 'rel'}) decode "
+          f"{err['decode']:.2e}, prefill {err['prefill']:.2e}, lse (abs) {err['lse']:.2e}", flush=True)

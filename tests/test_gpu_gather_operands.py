@@ -1,0 +1,119 @@
+"""Bit-exact page-gather indexing of the attention kernels' own loaders.
+
+paged_kv_debug_gather_operands runs the matrix-core kernels' page loaders over every
+cached token -- path 0 the decode block pipeline (page window in a register, buffer
+descriptors, blocks in flight; per-token table lookups on pages of 8 and 16), path 1
+the prefill kernel's LDS staging (a workgroup fetches and decodes each block, the waves
+read it back with their operand lane map) -- and writes the K and V operands back in
+logical order.  They must equal, bit for bit, the oracle's plain gather (page =
+table[t // P], slot t % P) of the same pool: bf16 values as stored, FP8 codes widened
+exactly, MXFP4 elements times their block scale ("NVIDIA TensorRT-LLM详解：架构、KV
+Cache、调度与部署实践", §9: logical blocks map to physical blocks through the table)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.oracle_state import oracle_pool
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC1  # a NaN pattern no operand takes: rows past a sequence must keep it
+
+# (name, cache dtype, page size, head_dim, G): lengths 1..700 cross pages, the 64-page
+# register window (pages of 8) and ragged last blocks
+CASES = []
+for kv in ("bf16", "fp8"):
+    for P in (8, 16, 32, 64, 128):
+        CASES.append((kv, P, 128))
+    CASES += [(kv, 32, 64), (kv, 128, 64)]
+CASES += [("mxfp4", 32, 128), ("mxfp4", 64, 128), ("mxfp4", 128, 128), ("mxfp4", 32, 64), ("mxfp4", 64, 64)]
+
+
+def _bf16_bits_exact(x):
+    """float64 values that are bf16 values -> their bf16 bit patterns (asserts exactness)."""
+    f = x.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), x)
+    u = f.view(np.uint32)
+    assert not (u & 0xFFFF).any(), "a value is not a bf16 value"
+    return (u >> 16).astype(np.uint16)
+
+
+def _expected(wl, pool, s, L, g):
+    """Oracle gather of sequence s, kv head g, with unit FP8 scales (the kernels apply the
+    per-head scales to the products, not to the operands)."""
+    ones = np.ones(wl.num_kv_heads, np.float32)
+    K, V = oracle.gather(pool, wl.block_tables[s], L, g, wl.kv_dtype, ones, ones)
+    return _bf16_bits_exact(K), _bf16_bits_exact(V)
+
+
+@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("kv,P,D", CASES, ids=lambda x: str(x))
+def test_hot_path_gather_is_bit_exact(gpu_lib, kv, P, D, path):
+    from paged_kv_cache_413_amd import binding as B
+    from tests.device_batch import DeviceBatch
+    if path == 1 and P < 32:
+        pytest.skip("the prefill staging serves pages of >= 32 tokens (shorter pages use the decode loaders)")
+    hkv = 2 if D == 64 else 4
+    wl = workloads.make(2, num_seqs=6, len_range=(1, 700), page_size=P, head_dim=D, num_kv_heads=hkv,
+                        num_q_heads=4 * hkv, kv_dtype=kv)
+    print(f"[case] operands path={path} kv={kv} P={P} D={D} lens={wl.context_lens.tolist()}", flush=True)
+    db = DeviceBatch(wl)
+    db.fill_history()
+    db.prepare_step()
+    db.append_step()
+    S, Lm, H = wl.num_seqs, wl.max_context_len, wl.num_kv_heads
+    kout = torch.full((S, Lm, H, D), SENTINEL, dtype=torch.int16, device=db.dev)
+    vout = kout.clone()
+    B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, path, kout, vout)
+    torch.cuda.synchronize()
+    kg, vg = kout.cpu().numpy().view(np.uint16), vout.cpu().numpy().view(np.uint16)
+    pool = oracle_pool(wl)
+    for s in range(S):
+        L = int(wl.context_lens[s])
+        for g in range(H):
+            ek, ev = _expected(wl, pool, s, L, g)
+            assert np.array_equal(kg[s, :L, g], ek), f"K of seq {s} head {g}: {int((kg[s, :L, g] != ek).sum())} differ"
+            assert np.array_equal(vg[s, :L, g], ev), f"V of seq {s} head {g}: {int((vg[s, :L, g] != ev).sum())} differ"
+        assert (kg[s, L:] == SENTINEL).all() and (vg[s, L:] == SENTINEL).all(), f"seq {s}: rows past L written"
+
+
+def test_hot_path_gather_after_page_permutation(gpu_lib):
+    """The same logical tokens behind permuted physical pages load the same operands."""
+    from paged_kv_cache_413_amd import binding as B
+    from tests.device_batch import DeviceBatch
+    outs = []
+    for perm_seed in (None, 3):
+        wl = workloads.make(2, num_seqs=5, len_range=(40, 500), page_size=32)
+        if perm_seed is not None:
+            perm = np.random.default_rng(perm_seed).permutation(wl.num_pages)
+            bt = wl.block_tables
+            wl.block_tables = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+        db = DeviceBatch(wl)
+        db.fill_history()
+        db.prepare_step()
+        db.append_step()
+        S, Lm, H, D = wl.num_seqs, wl.max_context_len, wl.num_kv_heads, wl.head_dim
+        res = []
+        for path in (0, 1):
+            k = torch.zeros((S, Lm, H, D), dtype=torch.int16, device=db.dev)
+            v = torch.zeros_like(k)
+            B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, path, k, v)
+            res += [k, v]
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in res])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_operands_reject_unsupported_caches(gpu_lib):
+    from paged_kv_cache_413_amd import binding as B
+    from tests.device_batch import DeviceBatch
+    wl = workloads.make(1)   # an f32 cache: no matrix-core loader
+    db = DeviceBatch(wl)
+    db.prepare_step()
+    k = torch.zeros(16, dtype=torch.int16, device=db.dev)
+    with pytest.raises(B.PagedKVError) as e:
+        B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, 0, k, k)
+    assert e.value.code == B.PKV_EUNSUPPORTED

@@ -25,7 +25,7 @@ SMALL = {
 
 
 def _batch(gpu_lib, name, num_splits=None, **extra):
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     cfg, over = SMALL[name]
     wl = workloads.make(cfg, **{**over, **extra})
     print(f"[case] {name} S={wl.num_seqs} Lmax={wl.max_context_len} kv={wl.kv_dtype}", flush=True)
@@ -53,7 +53,7 @@ def test_append_routes_rows_across_many_sequences(gpu_lib, kv):
     owner is found in two rounds) where only every third sequence has a new row: each
     row lands in its own sequence's slot and sequences without rows keep their bytes."""
     from paged_kv_cache_413_amd import binding as B
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch, to_device
+    from tests.device_batch import DeviceBatch, to_device
     wl = workloads.make(2, num_seqs=300, len_range=(2, 90), kv_dtype=kv)
     print(f"[case] sparse append S={wl.num_seqs} kv={kv}", flush=True)
     db = DeviceBatch(wl)
@@ -141,7 +141,7 @@ def test_page_permutation_is_bit_identical(gpu_lib, name):
     bt = wl.block_tables
     wl2 = workloads.make(SMALL[name][0], **SMALL[name][1])
     wl2.block_tables = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     db2 = DeviceBatch(wl2)
     db2.fill_history()
     db2.step()
@@ -154,7 +154,7 @@ def test_page_permutation_is_bit_identical(gpu_lib, name):
 
 def test_edge_lengths_and_tiny_pages(gpu_lib):
     """Lengths 1, P-1, P, P+1 and a 2-token page size."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     for P, lens in ((2, [1, 2, 3, 5, 64]), (16, [1, 15, 16, 17, 33]), (64, [1, 63, 64, 65, 300])):
         wl = workloads.make(1, lens=lens, page_size=P, num_pages=-(-max(lens) // P) * len(lens) + 3)
         print(f"[case] edge P={P} lens={lens}", flush=True)
@@ -173,7 +173,7 @@ def test_edge_lengths_and_tiny_pages(gpu_lib):
 def test_one_hot_probe_checks_gather_through_attention(gpu_lib):
     """A query aligned with one key that is far larger than the rest returns exactly
     that key's V row: the attention kernel read the right slot of the right page."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(2, num_seqs=3, len_range=(200, 500))
     db = DeviceBatch(wl)
     db.fill_history()
@@ -220,7 +220,7 @@ def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
     """The matrix-core decode kernels on ragged lengths around page and 32-token
     block edges, pages of 8..128 tokens, groups of 1..16 query heads per kv head,
     head_dim 64 and 128, balanced and fixed partitions."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(2, lens=lens, page_size=P, num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
                         num_splits=ns)
     print(f"[case] mfma edge P={P} lens={lens} Hq={hq} Hkv={hkv} D={D} splits={ns}", flush=True)
@@ -239,7 +239,7 @@ def test_many_short_sequences(gpu_lib, kv, num_seqs, splits):
     """Thousands of decode sequences of 1..80 tokens (Llama-3-8B heads, pages of 64):
     the balanced schedule's search over sequences runs many 64-sequence rounds and its
     shares hold many whole segments; fixed partitions give most sequences one."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(2, num_seqs=num_seqs, len_range=(1, 80), kv_dtype=kv, num_splits=splits)
     print(f"[case] many sequences S={num_seqs} kv={kv} splits={splits}", flush=True)
     db = DeviceBatch(wl)
@@ -270,12 +270,12 @@ AUTO_WAVES = [
 
 
 @pytest.mark.parametrize("waves,cfg,over", AUTO_WAVES)
-def test_auto_decode_few_waves(gpu_lib, monkeypatch, waves, cfg, over):
-    """The balanced decode schedule with few waves (PKV_AUTO_WAVES): long shares that
+def test_auto_decode_few_waves(gpu_lib, auto_waves, waves, cfg, over):
+    """The balanced decode schedule with few waves (the test-only wave override): long shares that
     cross many segment boundaries and segments cut over several waves match the
     oracle, and a second call gives the same bits."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
-    monkeypatch.setenv("PKV_AUTO_WAVES", str(waves))
+    from tests.device_batch import DeviceBatch
+    auto_waves(waves)
     wl = workloads.make(cfg, num_splits=0, **over)
     print(f"[case] auto waves={waves} cfg={cfg} {over}", flush=True)
     db = DeviceBatch(wl)
@@ -305,16 +305,16 @@ SHORT_CHUNKS = [
 
 
 @pytest.mark.parametrize("waves,P,chunks,cached,hq,hkv,D", SHORT_CHUNKS)
-def test_short_chunks_via_decode_kernels(gpu_lib, monkeypatch, waves, P, chunks, cached, hq, hkv, D):
+def test_short_chunks_via_decode_kernels(gpu_lib, auto_waves, waves, P, chunks, cached, hq, hkv, D):
     """Prefill chunks of at most 16 / G queries (several tokens verified per sequence,
     as in speculative decoding) through paged_attn_prefill_chunk: all queries of a
     (sequence, kv head) share one MFMA tile of the decode kernels, each row with its
     causal limit; ragged chunk lengths, cut segments, every G that allows two or more
     queries per tile."""
     from paged_kv_cache_413_amd import binding as B
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     if waves:
-        monkeypatch.setenv("PKV_AUTO_WAVES", str(waves))
+        auto_waves(waves)
     wl = workloads.make(3, num_seqs=0, num_prefill=len(chunks), prefill_chunk=chunks, prefill_cached=cached,
                         page_size=P, num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
     print(f"[case] short chunks waves={waves} P={P} chunks={chunks} Hq={hq} Hkv={hkv} D={D}", flush=True)
@@ -357,7 +357,7 @@ def test_prefill_edge_shapes(gpu_lib, P, chunks, cached, hq, hkv, D):
     masks), chunks of 1 and around the 16-row tile and 32-key block edges, groups of
     1..16 query heads, head_dim 64 and 128, pages of 8..128, and enough queries for
     several waves per (sequence, kv head) and for key splits to be merged."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(3, num_seqs=len(chunks) + 2, num_prefill=len(chunks), prefill_chunk=chunks,
                         prefill_cached=cached, median=50, clip=(1, 300), page_size=P,
                         num_q_heads=hq, num_kv_heads=hkv, head_dim=D)
@@ -378,12 +378,14 @@ def test_step_replays_from_a_captured_graph(gpu_lib, chunks):
     """A whole step (kv_append, prefill-chunk attention, decode attention and their
     merges) captured in a HIP graph and replayed three times, with eager kernels that
     overwrite every output in between: each replay reproduces the eager results bit for
-    bit (the library allocates nothing and enqueues no memset, so the step captures
-    as is).  Query-tiled prefill chunks and short chunks on the decode kernels."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    bit and matches the oracle (the library allocates nothing and enqueues no memset,
+    so the step captures as is).  Query-tiled prefill chunks and short chunks on the decode kernels."""
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(3, num_seqs=6, num_prefill=len(chunks), prefill_chunk=chunks,
                         prefill_cached=[190, 40, 700][:len(chunks)], median=300, clip=(1, 900))
     print(f"[case] graph replay chunks={chunks}", flush=True)
+    ref_pool = oracle_pool(wl)
+    ref = oracle_outputs(wl, ref_pool)
     db = DeviceBatch(wl)
     db.fill_history()
     db.prepare_step()
@@ -412,6 +414,14 @@ def test_step_replays_from_a_captured_graph(gpu_lib, chunks):
         for name, t, e in zip(("decode out", "decode lse", "prefill out", "prefill lse"), outs, eager):
             assert torch.equal(bits(t), e), f"replay {rep}: {name}"
         assert torch.equal(db.pool.view(torch.int16), pool_eager), f"replay {rep}: pool"
+        # and each replay's results against the oracle, not only against the eager run
+        dec, dec_lse, pf, pf_lse = db.outputs_f64()
+        assert_close(dec, ref[0], wl.kv_dtype, f"replay {rep}: decode")
+        assert_lse_close(dec_lse, ref[1], wl.kv_dtype, f"replay {rep}: decode")
+        assert_close(pf, ref[2], wl.kv_dtype, f"replay {rep}: prefill")
+        assert_lse_close(pf_lse, ref[3], wl.kv_dtype, f"replay {rep}: prefill")
+        assert np.array_equal(pool_token_major(db.pool_bits()).view(np.uint8), ref_pool.view(np.uint8)), \
+            f"replay {rep}: pool differs from the oracle's"
 
 
 WINDOWS = [
@@ -438,7 +448,7 @@ def test_window_matches_oracle_after_page_release(gpu_lib, cfg, over, W):
     are released: their table entries set to -1 and their contents overwritten with
     NaN.  The result still matches the oracle: nothing before a window is read."""
     from paged_kv_cache_413_amd import page_table
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(cfg, window=W, **over)
     print(f"[case] window W={W} cfg={cfg} {over}", flush=True)
     db = DeviceBatch(wl)
@@ -553,7 +563,7 @@ FP8_PREFILL = [
 def test_fp8_prefill_matches_oracle(gpu_lib, P, chunks, cached, hq, hkv, D, W):
     """Prefill-chunk attention over an FP8 (E4M3) cache with per-kv-head scales, on
     each prefill path, decode rows in the same batch."""
-    from paged_kv_cache_413_amd.device_batch import DeviceBatch
+    from tests.device_batch import DeviceBatch
     wl = workloads.make(3, num_seqs=4, num_prefill=len(chunks), prefill_chunk=chunks, prefill_cached=cached,
                         median=200, clip=(1, 600), page_size=P, num_q_heads=hq, num_kv_heads=hkv,
                         head_dim=D, kv_dtype="fp8", window=W)

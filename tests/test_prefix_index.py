@@ -20,11 +20,11 @@ def test_partial_match_of_the_next_page_is_reported_for_copying():
     assert m.pages == [40, 41] and (m.partial_page, m.partial_tokens) == (42, 2)
 
 
-def test_salt_isolates_tenants():
+def test_a_full_page_match_is_not_a_partial_match():
     idx = PrefixIndex(P)
-    idx.insert(SYS, [40, 41], salt="tenant-a")
-    assert idx.match(SYS, salt="tenant-b").pages == []
-    assert idx.match(SYS, salt="tenant-a").pages == [40, 41]
+    idx.insert(SYS, [40, 41])
+    m = idx.match(SYS[:4] + [5, 6, 7, 8])
+    assert m.pages == [40, 41] and m.partial_page == -1
 
 
 def test_duplicate_insert_keeps_the_tree_page():
@@ -32,17 +32,11 @@ def test_duplicate_insert_keeps_the_tree_page():
     idx.insert(SYS, [40, 41])
     assert idx.insert(SYS + [1, 1, 1, 1], [50, 51, 52]) == [50, 51]
     assert idx.match(SYS + [1, 1, 1, 1]).pages == [40, 41, 52]
+    assert len(idx) == 3
 
 
-def test_eviction_takes_free_leaves_by_priority_then_age():
+def test_divergence_in_the_first_page_matches_nothing_whole():
     idx = PrefixIndex(P)
-    idx.insert(SYS + [9, 9, 9, 9], [40, 41, 42], priority=35)
-    idx.insert(SYS + [7, 7, 7, 7], [40, 41, 43], priority=80)     # shares 40, 41
-    idx.insert([5, 5, 5, 5], [44], priority=35)
-    m = idx.match(SYS + [9, 9, 9, 9])                              # a request holds 40, 41, 42
-    # free leaves: 43 (priority 80), 44 (priority 35, newer than 42 but 42 is held)
-    assert idx.evict(1) == [44]
-    assert idx.evict(5) == [43]                 # 42 held; 40, 41 are not leaves while 42 stays
-    idx.release(m.pages)
-    assert idx.evict(5) == [42, 41, 40]         # the chain unwinds leaf by leaf
-    assert len(idx) == 0
+    idx.insert(SYS, [40, 41])
+    m = idx.match([1, 2, 0, 0] + SYS[4:])
+    assert m.pages == [] and (m.partial_page, m.partial_tokens) == (40, 2)
