@@ -48,13 +48,15 @@ def _expected(wl, pool, s, L, g):
     return _bf16_bits_exact(K), _bf16_bits_exact(V)
 
 
-@pytest.mark.parametrize("path", [0, 1])
-@pytest.mark.parametrize("kv,P,D", CASES, ids=lambda x: str(x))
+# path 1 (the prefill staging) serves pages of >= 32 tokens; shorter pages prefill
+# through the decode loaders of path 0
+PATH_CASES = [(kv, P, D, path) for (kv, P, D) in CASES for path in (0, 1) if path == 0 or P >= 32]
+
+
+@pytest.mark.parametrize("kv,P,D,path", PATH_CASES, ids=lambda x: str(x))
 def test_hot_path_gather_is_bit_exact(gpu_lib, kv, P, D, path):
     from paged_kv_cache_413_amd import binding as B
     from tests.device_batch import DeviceBatch
-    if path == 1 and P < 32:
-        pytest.skip("the prefill staging serves pages of >= 32 tokens (shorter pages use the decode loaders)")
     hkv = 2 if D == 64 else 4
     wl = workloads.make(2, num_seqs=6, len_range=(1, 700), page_size=P, head_dim=D, num_kv_heads=hkv,
                         num_q_heads=4 * hkv, kv_dtype=kv)
