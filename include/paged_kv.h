@@ -217,6 +217,23 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
                       int32_t num_splits, void* out, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* paged_attn_decode_noalloc -- paged_attn_decode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same call without a workspace argument.  Its workspace is
+ * a device array the library owns, PKV_NOALLOC_SCRATCH_BYTES per device, held from
+ * the moment the library is loaded on a device until the process ends; the call
+ * allocates nothing.  Same arguments, kernels and results as paged_attn_decode (bit
+ * for bit).  PKV_EWORKSPACE when the call's plan needs more than the array holds
+ * (paged_attn_decode_workspace_size gives the need: about 4.2 MB for a 64-sequence,
+ * 32/8-head, head_dim 128 decode batch; 8.5 MB for 8 sequences in 64 fixed
+ * partitions).  Every call on one device shares that device's array, and the array
+ * keeps the last call's partial results: calls that overlap in time on one device
+ * (several streams, or several host threads) race and must not be issued. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paged_attn_decode_noalloc(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const void* q,
+                              int32_t q_dtype, int32_t num_q_heads, float sm_scale,
+                              int32_t num_splits, void* out, float* lse_out, void* stream);
+
 /* paged_attn_prefill_chunk -- causal attention of prompt chunks against the cache
  * the chunks were just appended to ([Deep dive] §8, chunked prefill: every chunk
  * but the last is a multiple of the block size; §6: context requests are packed

@@ -26,7 +26,7 @@ TORCH_DTYPE = {PKV_F32: torch.float32, PKV_BF16: torch.bfloat16, PKV_FP8_E4M3: t
 DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
 EXPORTS = ("paged_kv_page_bytes", "kv_append", "kv_copy_pages", "paged_attn_decode_workspace_size",
-           "paged_attn_decode", "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
+           "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
            "paged_kv_debug_gather", "paged_kv_debug_gather_operands", "paged_kv_debug_status",
            "paged_kv_debug_set_auto_waves", "paged_kv_last_error")
 
@@ -76,6 +76,9 @@ def load(path: str = LIB_PATH):
     lib.paged_attn_decode.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
                                       c_int32, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.paged_attn_decode.restype = c_int32
+    lib.paged_attn_decode_noalloc.argtypes = [P(PkvCache), P(PkvSeqs), c_void_p, c_int32, c_int32, c_float,
+                                              c_int32, c_void_p, c_void_p, c_void_p]
+    lib.paged_attn_decode_noalloc.restype = c_int32
     lib.paged_attn_prefill_workspace_size.argtypes = [P(PkvCache), P(PkvSeqs), c_int32, c_int32,
                                                       c_int32, c_int32]
     lib.paged_attn_prefill_workspace_size.restype = c_size_t
@@ -177,6 +180,16 @@ def paged_attn_decode(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, num_q_hea
                                     int(num_q_heads), float(sm_scale), int(num_splits), _ptr(out),
                                     _ptr(lse_out), _ptr(workspace), int(workspace_bytes),
                                     _stream(stream)))
+
+
+def paged_attn_decode_noalloc(cache: PkvCache, seqs: PkvSeqs, q, q_dtype: int, num_q_heads: int,
+                              sm_scale: float, num_splits: int, out, lse_out=None, stream=None):
+    _check(load().paged_attn_decode_noalloc(ctypes.byref(cache), ctypes.byref(seqs), _ptr(q), int(q_dtype),
+                                            int(num_q_heads), float(sm_scale), int(num_splits), _ptr(out),
+                                            _ptr(lse_out), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 def paged_attn_prefill_workspace_size(cache: PkvCache, seqs: PkvSeqs, q_dtype: int,

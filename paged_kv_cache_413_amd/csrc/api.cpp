@@ -65,6 +65,17 @@ int cu_count() {
 }  // namespace
 
 namespace pkv {
+// The error reporting of the front end, for entry points defined in other sources.
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
 int resident_blocks(const void* kernel, int block) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
