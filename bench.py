@@ -14,9 +14,18 @@ and V of every attended token of every decode sequence) per second of wall-clock
 time over K uninstrumented steps.  Then each call of the step runs K times back to back
 between two HIP events on the launch stream: `kernel_us` lists the mean duration of
 each call, and `roofline` rates the dominant one, paged_attn_decode (its attention
-kernel plus its merge kernel), against MI355X's 8 TB/s HBM peak.
-`kernel_us_cold_caches` gives the attention calls again, each alone after a 1 GiB write
-that evicts L2 and the Infinity Cache (median of K).
+kernel plus its merge kernel), against MI355X's 8 TB/s HBM peak, on its algorithmic
+bytes (K and V of every attended token once; a page that several sequences share counts
+once, the per-sequence figure is given beside it as `*_logical`), and against the
+library's plain streaming read of as many bytes (`stream_read`, measured in the same
+run).  A workload with both prefill chunks and decode sequences also gets
+`roofline_prefill`: the prefill call's exact causal flops against the 2.5 PFLOP/s dense
+bf16 matrix-core peak.  `kernel_us_cold_caches` gives the attention calls again, each
+alone after a 1 GiB write that evicts L2 and the Infinity Cache (median of K), and
+`step_us` the whole step that way (median and min of K); the `frac_cold_median` figures
+rate those.  `memory` compares the pages the batch holds with a static reservation of
+the longest context per sequence.  `traffic` is the HBM bytes per launch from rocprofv3
+counters (profiles/), while the kernel sources still hash to the record's.
 `cpu_baseline` is the CPU fp64 oracle timed on a bounded sample of the same workload
 on the host cores.
 """
@@ -35,6 +44,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0   # dense bf16 matrix-core peak (the products run in bf16)
 WORKLOADS = {
     "llama3_8b_decode_bf16": 2,
     "tiny_fp32_decode": 1,
@@ -65,17 +75,20 @@ def compute_dtype(wl) -> str:
 def kv_bytes_per_elem(kv_dtype: str) -> float:
     """Cache bytes per K or V element (MXFP4: half a byte plus a scale byte per 32)."""
     return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 17.0 / 32.0}[kv_dtype]
-# sources of the decode call on the matrix-core path (the traffic record is void once any changes)
-KERNEL_SOURCES = ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp",
-                  "../build.py")  # (the compile flags too)
+# sources of the rated calls on the matrix-core path (a traffic record is void once any changes)
+KERNEL_SOURCES = {
+    "decode": ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp", "../build.py"),
+    "prefill": ("prefill_mfma.hip", "stage.h", "mfma_common.h", "device_common.h", "internal.h", "api.cpp",
+                "../build.py"),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str = "decode") -> str:
     """Hash of those sources with comments and blank space removed: an edit that only
     touches comments leaves the compiled kernels, and so the record, as they were."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_413_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kind]:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
             text = open(p).read()
@@ -86,16 +99,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per decode launch measured with rocprofv3 counters, if the summary
-    under profiles/ was taken from the kernel sources as they are now."""
-    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.md")
+def recorded_traffic(workload: str, kind: str = "decode"):
+    """HBM bytes per launch of the rated call measured with rocprofv3 counters
+    (profiles/<kind>_traffic_<workload>.md), if that record was taken from the kernel
+    sources as they are now."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", text)
     m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_src and m_val) or m_src.group(1) != kernel_source_hash():
+    if not (m_src and m_val) or m_src.group(1) != kernel_source_hash(kind):
         return None
     return float(m_val.group(1))
 
@@ -124,6 +138,71 @@ def algorithmic_bytes(wl) -> dict:
     qo = 2 * nq * wl.num_q_heads * wl.head_dim * qel
     bt = int(((L + wl.page_size - 1) // wl.page_size).sum()) * 4 + len(rows) * 4
     return {"kv": kv, "total": kv + qo + bt}
+
+
+def unique_kv_tokens(wl, rows) -> int:
+    """Distinct (page, slot) pairs the rows' attended keys occupy: a page that several
+    sequences share (a common prefix) counts once -- the bytes HBM must deliver at least."""
+    import numpy as np
+    P = wl.page_size
+    keys = []
+    for s in rows:
+        L, n = int(wl.context_lens[s]), int(wl.new_lens[s])
+        lo = max(0, L - n - wl.window + 1) if wl.window > 0 else 0
+        t = np.arange(lo, L, dtype=np.int64)
+        keys.append(wl.block_tables[s][t // P].astype(np.int64) * P + t % P)
+    return int(np.unique(np.concatenate(keys)).size) if keys else 0
+
+
+def prefill_flops(wl) -> int:
+    """Exact causal flops of the prefill call: 4 * D per (query row, head, visible key),
+    query i of a chunk of C at position L - C + i seeing keys window_lo .. its own."""
+    import numpy as np
+    total = 0
+    for s in range(wl.num_prefill):
+        L, C = int(wl.context_lens[s]), int(wl.new_lens[s])
+        pos = np.arange(L - C, L, dtype=np.int64)
+        lo = np.maximum(0, pos - wl.window + 1) if wl.window > 0 else np.zeros_like(pos)
+        total += int((pos + 1 - lo).sum())
+    return total * 4 * wl.head_dim * wl.num_q_heads
+
+
+def memory_report(wl) -> dict:
+    """Paged KV memory against a static reservation of max_seq_len (the batch's longest
+    context) per sequence -- the page count paging saves."""
+    import numpy as np
+    P = wl.page_size
+    logical = int(((wl.context_lens.astype(np.int64) + P - 1) // P).sum())
+    unique = int(wl.referenced_pages().size)
+    static = int(wl.num_seqs * -(-int(wl.context_lens.max()) // P))
+    page_bytes = 2 * wl.num_kv_heads * P * wl.head_dim * kv_bytes_per_elem(wl.kv_dtype)
+    return {"page_tokens": P, "pages_paged": unique, "pages_paged_without_sharing": logical,
+            "pages_static_reservation": static, "bytes_paged": int(unique * page_bytes),
+            "bytes_static_reservation": int(static * page_bytes),
+            "saving": round(1.0 - unique / static, 4)}
+
+
+def stream_read(nbytes: int, reps: int):
+    """The library's plain streaming read of nbytes (the decode launch shape), reps times
+    back to back between two HIP events on the launch stream: GB/s."""
+    import torch
+    from paged_kv_cache_413_amd import binding
+    nbytes = nbytes // 1024 * 1024
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(binding.paged_kv_stream_read_waves(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        binding.paged_kv_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        binding.paged_kv_stream_read(buf, nbytes, sink)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    del buf
+    return {"bytes": nbytes, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -262,6 +341,9 @@ def main():
     ap.add_argument("--page-copy", type=int, default=0,
                     help="only time kv_copy_pages on this many page pairs of the workload's pool "
                          "(K steps back to back between two events), print its JSON line, exit")
+    ap.add_argument("--stream-read-mb", type=float, default=0.0,
+                    help="only time the library's plain streaming read of this many MB (the "
+                         "practical HBM-read ceiling), --steps times back to back, print its JSON line, exit")
     ap.add_argument("--copy-mb", type=float, default=0.0,
                     help="only run a plain device-to-device copy of this many MB, --steps times "
                          "(the known-size reference for the HBM byte counters), then exit")
@@ -290,6 +372,12 @@ def main():
         print(json.dumps({"copy_bytes": n, "steps": args.steps}), flush=True)
         return
     binding.load()  # raises when libpagedkv.so is missing: there is no other path
+    if args.stream_read_mb > 0:
+        r = stream_read(int(args.stream_read_mb * 1e6), args.steps)
+        print(json.dumps({"metric": "plain streaming read of a device buffer (paged_kv_stream_read)",
+                          "value": r["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                          "higher_is_better": True, "data": "synthetic", **r}), flush=True)
+        return
 
     if args.page_copy > 0:
         page_copy_bench(make_workload(args.workload), args.page_copy, args.steps, args.warmup)
@@ -357,20 +445,39 @@ def main():
 
     cold = {"paged_attn_prefill_chunk": round(cold_call_us(db.prefill_step), 2) if wl.num_prefill else None,
             "paged_attn_decode": round(cold_call_us(db.decode_step), 2) if wl.num_prefill < wl.num_seqs else None}
+    # whole steps with cold caches (the flushed protocol): median and min of K
+    step_cold = []
+    for _ in range(K):
+        flush.fill_(1)
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record()
+        db.step()
+        b.record()
+        torch.cuda.synchronize()
+        step_cold.append(a.elapsed_time(b) * 1e3)
     del flush
     fmt = lambda us: "-" if us is None else f"{us:.1f} us"
     print(f"[bench] step {ms_step * 1e3:.1f} us; per call: append {append_us:.1f} us, prefill "
           f"{fmt(prefill_us)}, decode {fmt(decode_us)}", file=sys.stderr, flush=True)
 
     ab = algorithmic_bytes(wl)
+    rows = attention_rows(wl)
+    uniq_kv = unique_kv_tokens(wl, rows) * 2 * wl.num_kv_heads * wl.head_dim * kv_bytes_per_elem(wl.kv_dtype)
+    shared = uniq_kv < ab["kv"]
     tokens = int(wl.new_lens.sum())
     kv_gbs = ab["kv"] / (ms_step * 1e-3) / 1e9
     # the measured attention call: decode, or the prefill call of a chunks-only workload
     prefill_only = wl.num_prefill == wl.num_seqs
     call = "paged_attn_prefill_chunk" if prefill_only else "paged_attn_decode"
     call_us = prefill_us if prefill_only else decode_us
-    achieved = ab["total"] / (call_us * 1e-6) / 1e9
+    # the rated call's algorithmic bytes: K and V of every attended token once -- a page
+    # that several sequences share counted once (what HBM must deliver at least), the
+    # per-sequence (logical) figure beside it
+    alg = int(ab["total"] - ab["kv"] + uniq_kv) if shared else ab["total"]
+    achieved = alg / (call_us * 1e-6) / 1e9
+    call_cold = cold[call]
     traffic = recorded_traffic(wl.name)
+    sr = stream_read(max(ab["kv"], 256 << 20), K)
 
     # one decode launch through the split count the bench used, for the record
     ns = db.num_splits
@@ -399,12 +506,32 @@ def main():
                       "paged_attn_prefill_chunk": None if prefill_us is None else round(prefill_us, 2),
                       "paged_attn_decode": None if decode_us is None else round(decode_us, 2)},
         "kernel_us_cold_caches": cold,
+        "step_us": {"timed_loop_mean": round(ms_step * 1e3, 2),
+                    "cold_median": round(float(np.median(step_cold)), 2),
+                    "cold_min": round(float(np.min(step_cold)), 2)},
         "roofline": {"bound": "hbm", "kernel": call,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": ab["total"]},
-        "kernel_source_hash": kernel_source_hash(),
+                     "frac_cold_median": round(alg / (call_cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_of_stream_read": round(achieved / sr["gbs"], 4),
+                     "traffic": traffic, "algorithmic_bytes": alg},
+        "stream_read": sr,
+        "memory": memory_report(wl),
+        "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
     }
+    if shared:
+        lg = ab["total"] / (call_us * 1e-6) / 1e9
+        res["roofline"].update({"algorithmic_bytes_logical": ab["total"], "achieved_logical": round(lg, 2),
+                                "frac_logical": round(lg / HBM_PEAK_GBS, 4)})
+    if wl.num_prefill and not prefill_only:
+        fl = prefill_flops(wl)
+        tf = fl / (prefill_us * 1e-6) / 1e12
+        res["roofline_prefill"] = {"bound": "mfma", "kernel": "paged_attn_prefill_chunk",
+                                   "achieved": round(tf, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                                   "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                                   "frac_cold_median": round(fl / (cold["paged_attn_prefill_chunk"] * 1e-6) / 1e12
+                                                             / MFMA_BF16_PEAK_TFS, 4),
+                                   "flops": fl, "traffic": recorded_traffic(wl.name, "prefill")}
     del db
     torch.cuda.empty_cache()
     if args.cpu_budget > 0:

@@ -296,6 +296,16 @@ int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void
 int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* seqs, int32_t path,
                                    void* k_out, void* v_out, void* stream);
 
+/* paged_kv_stream_read -- measurement helper: read `bytes` of a device buffer once, at
+ * the decode kernels' launch shape (one 64-lane wave per SIMD, 16-byte non-temporal loads,
+ * eight 1 KiB loads in flight per wave), and write one word per wave to `sink`.  Its rate
+ * is the practical HBM-read ceiling the attention kernels are compared with.
+ *   src: 1024-byte aligned; bytes: a multiple of 1024.
+ *   sink: device buffer of paged_kv_stream_read_waves() 32-bit words (contents meaningless). */
+int paged_kv_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+/* Waves (and sink words) of paged_kv_stream_read on the current device (<= 16384). */
+int32_t paged_kv_stream_read_waves(void);
+
 /* Contract violations found by device validation (PKV_DEBUG=1), as bits. */
 typedef enum {
   PKV_DEBUG_PAGE_RANGE = 1,  /* a page id the call addresses is outside [0, num_pages) */

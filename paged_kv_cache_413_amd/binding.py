@@ -28,7 +28,8 @@ DTYPE_OF = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 EXPORTS = ("paged_kv_page_bytes", "kv_append", "kv_copy_pages", "paged_attn_decode_workspace_size",
            "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_prefill_workspace_size", "paged_attn_prefill_chunk",
            "paged_kv_debug_gather", "paged_kv_debug_gather_operands", "paged_kv_debug_status",
-           "paged_kv_debug_set_auto_waves", "paged_kv_last_error")
+           "paged_kv_debug_set_auto_waves", "paged_kv_stream_read", "paged_kv_stream_read_waves",
+           "paged_kv_last_error")
 
 # device-validation bits (PKV_DEBUG=1), as paged_kv_debug_status reports them
 PKV_DEBUG_PAGE_RANGE, PKV_DEBUG_LENGTH, PKV_DEBUG_CU, PKV_DEBUG_DUP_SLOT, PKV_DEBUG_COPY_PAIRS = 1, 2, 4, 8, 16
@@ -92,6 +93,10 @@ def load(path: str = LIB_PATH):
     lib.paged_kv_debug_gather_operands.restype = c_int32
     lib.paged_kv_debug_status.argtypes = [c_int32]
     lib.paged_kv_debug_status.restype = c_int32
+    lib.paged_kv_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+    lib.paged_kv_stream_read.restype = c_int32
+    lib.paged_kv_stream_read_waves.argtypes = []
+    lib.paged_kv_stream_read_waves.restype = c_int32
     lib.paged_kv_debug_set_auto_waves.argtypes = [c_int32]
     lib.paged_kv_debug_set_auto_waves.restype = c_int32
     lib.paged_kv_last_error.argtypes = []
@@ -231,6 +236,14 @@ def paged_kv_debug_status(clear: bool = True) -> int:
 
 def paged_kv_debug_set_auto_waves(waves: int):
     _check(load().paged_kv_debug_set_auto_waves(int(waves)))
+
+
+def paged_kv_stream_read(src, nbytes: int, sink, stream=None):
+    _check(load().paged_kv_stream_read(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)))
+
+
+def paged_kv_stream_read_waves() -> int:
+    return int(load().paged_kv_stream_read_waves())
 
 
 def paged_kv_last_error() -> str:

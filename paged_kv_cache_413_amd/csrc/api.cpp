@@ -544,6 +544,23 @@ int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* s
   return launch_status(pkv::launch_debug_operands(c, s, path, k_out, v_out, hs), "paged_kv_debug_gather_operands");
 }
 
+// One wave per SIMD (four per compute unit), as the decode kernels run.
+int32_t paged_kv_stream_read_waves(void) {
+  ok();
+  return std::min(4 * cu_count(), 1 << 14);
+}
+
+int paged_kv_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(PKV_EINVAL, "src and sink must not be NULL");
+  if (!aligned(src, 1024) || bytes % 1024) return fail(PKV_EINVAL, "src must be 1024-byte aligned and bytes a multiple of 1024");
+  if (!aligned(sink, 4)) return fail(PKV_EINVAL, "sink must be 4-byte aligned");
+  if (bytes == 0) return ok();
+  return launch_status(pkv::launch_stream_read(src, int64_t(bytes), static_cast<uint32_t*>(sink),
+                                               std::min(4 * cu_count(), 1 << 14),
+                                               static_cast<hipStream_t>(stream)),
+                       "paged_kv_stream_read");
+}
+
 int32_t paged_kv_debug_status(int32_t clear) {
   int32_t bits = 0;
   const hipError_t e = pkv::read_debug_status(clear != 0, &bits);

@@ -114,6 +114,9 @@ hipError_t launch_copy_pages(const CacheArgs& c, const int32_t* src, const int32
 hipError_t launch_debug_gather(const CacheArgs& c, const SeqArgs& s, void* k_out, void* v_out,
                                hipStream_t stream);
 
+// Plain streaming read (stream_read.hip), one wave per workgroup.
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int waves, hipStream_t stream);
+
 // The attention kernels' own loaders over every cached token (debug_gather.hip): path 0
 // the decode block pipeline, path 1 the prefill kernel's LDS staging; bf16 operands out.
 bool operands_supported(int kv_dtype, int page_size, int head_dim, int path);
