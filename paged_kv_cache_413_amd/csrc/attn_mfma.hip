@@ -12,7 +12,9 @@
 //   scores^T [32 tok x 16 heads] = K [32 x D] . Q^T [D x 16]   -> 2 x D/32 MFMAs
 //   O        [16 heads x D]     += P [16 x 32 tok] . V [32 x D] -> D/16 MFMAs
 // Every operand comes straight from HBM in the register layout the MFMA wants:
-//   K tile of a page is token-major [P][D]: lane (m, c) loads 8 dims of one token row;
+//   K tile of a page is [D/32][P][32] (32-dim chunks, token-major inside a chunk):
+//   lane (m, c) loads 8 dims of one token row, and the 16 token rows of one load are
+//   one contiguous kilobyte;
 //   V tile of a page is dim-major inside 32-slot sub-blocks [P/32][D][32]: lane (n, c)
 //   loads 8 consecutive tokens of one dim, and the 16 dims of one load are one
 //   contiguous kilobyte -- so no LDS transpose sits on the hot path.

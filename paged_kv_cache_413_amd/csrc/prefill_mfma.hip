@@ -10,9 +10,11 @@
 // products run on the MFMA units.  The 16 MFMA rows of a tile are 16/G consecutive
 // queries x the G heads of one kv head; a wave carries kPrefillTiles tiles, so every
 // K/V block it loads (one 32-token block, straight into operand registers, the same
-// loads as decode) feeds kPrefillTiles x 16 rows (this per-wave kernel serves pages of
-// fewer than 32 tokens; other prefill runs on the LDS-shared kernel).  Causality is a per-row key limit,
-// applied only on the blocks that reach a row's position.
+// loads as decode) feeds kPrefillTiles x 16 rows.  This per-wave kernel serves pages of
+// fewer than 32 tokens and, on any page size, chunks that at most two waves' tiles
+// cover (mfma_prefill_geometry); other prefill runs on the LDS-shared kernel below.
+// Causality is a per-row key limit, applied only on the blocks that reach a row's
+// position.
 //
 // Work item (one wave): (sequence, kv head, key split, query tile).  When the chunk
 // alone does not give enough waves to fill the device, each tile's key range is cut
