@@ -77,18 +77,21 @@ def kv_bytes_per_elem(kv_dtype: str) -> float:
     return {"f32": 4.0, "bf16": 2.0, "fp8": 1.0, "mxfp4": 17.0 / 32.0}[kv_dtype]
 # sources of the rated calls on the matrix-core path (a traffic record is void once any changes)
 KERNEL_SOURCES = {
-    "decode": ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp", "../build.py"),
-    "prefill": ("prefill_mfma.hip", "stage.h", "mfma_common.h", "device_common.h", "internal.h", "api.cpp",
-                "../build.py"),
+    "decode": ("attn_mfma.hip", "mfma_common.h", "device_common.h", "internal.h", "api.cpp"),
+    "prefill": ("prefill_mfma.hip", "stage.h", "mfma_common.h", "device_common.h", "internal.h", "api.cpp"),
 }
 
 
 def kernel_source_hash(kind: str = "decode") -> str:
-    """Hash of those sources with comments and blank space removed: an edit that only
-    touches comments leaves the compiled kernels, and so the record, as they were."""
+    """Hash of those sources with comments and blank space removed, and of the compile
+    flags they are built with: an edit that only touches comments (or another source's
+    flags) leaves the compiled kernels, and so the record, as they were."""
+    from paged_kv_cache_413_amd import build as B
     h = hashlib.sha256()
+    h.update(" ".join(f for f in B.FLAGS if not f.startswith("-I")).encode())
     csrc = os.path.join(ROOT, "paged_kv_cache_413_amd", "csrc")
     for name in KERNEL_SOURCES[kind]:
+        h.update(" ".join(B.SOURCE_FLAGS.get(name, [])).encode())
         p = os.path.join(csrc, name)
         if os.path.exists(p):
             text = open(p).read()

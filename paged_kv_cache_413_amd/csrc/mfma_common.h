@@ -700,7 +700,7 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Blk& b, const flo
 // block (straight-line vector code), their sum into l, and the P operands pa.
 template <int D, int NT>
 __device__ __forceinline__ void softmax_head(State<D> (&st)[NT], const float (&sc)[NT][8], float scale,
-                                             float (&off)[NT], int lane) {
+                                             float (&off)[NT], int lane, f32x4* lsum = nullptr) {
   const int c = lane >> 4;
   bool grow[NT];
   float mref[NT];
@@ -728,12 +728,17 @@ __device__ __forceinline__ void softmax_head(State<D> (&st)[NT], const float (&s
       for (int dt = 0; dt < D / 16; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[r].o[dt][i] *= al[i];
+      if (lsum)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lsum[r][i] *= al[i];
       st[r].m = mref[r];
     }
   }
 }
 
-template <int NT, typename StateT>
+// SUM = false: the caller sums the weights itself (on the matrix cores, as a column of
+// P . 1 beside P . V), so l is left alone.
+template <int NT, bool SUM = true, typename StateT>
 __device__ __forceinline__ void softmax_tail(StateT (&st)[NT], const float (&sc)[NT][8], float scale,
                                              const float (&off)[NT], Frag8 (&pa)[NT]) {
 #pragma unroll
@@ -742,9 +747,9 @@ __device__ __forceinline__ void softmax_tail(StateT (&st)[NT], const float (&sc)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       p[e] = fast_exp2(__builtin_fmaf(sc[r][e], scale, off[r]));
-      ps += p[e];
+      if constexpr (SUM) ps += p[e];
     }
-    st[r].l += ps;
+    if constexpr (SUM) st[r].l += ps;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       pa[r].w[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p[2 * w], p[2 * w + 1]}, bf16x2));

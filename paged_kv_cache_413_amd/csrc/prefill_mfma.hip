@@ -43,25 +43,37 @@ struct PfGeom {
 
 // Finish the NT row tiles of a wave: rows of the chunk only.  One split: output and
 // log-sum-exp; several: partial record (row, kv head, split) for the merge kernel.
+// lsum: NULL, or each tile's sums of the weights in the O layout (lane (n, c) holds those
+// of rows 4c .. 4c+3, in every column n), summed on the matrix cores; else st[r].l holds
+// the lane's share of its row's sum.
 template <int D, int G, int NT>
 __device__ __forceinline__ void prefill_finish(const AttnArgs& a, const State<D> (&st)[NT], int q0, int C,
                                                int cq0, int g, int split, float qk_scale, float vscale,
-                                               int lane) {
+                                               int lane, const f32x4* lsum = nullptr) {
   constexpr int QPT = PfGeom<G>::QPT;
   const int n = lane & 15, c = lane >> 4;
   const int Hkv = a.cache.num_kv_heads, Hq = a.num_q_heads, nsplit = a.max_splits;
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    float l = st[r].l;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    const float lse = row_lse(st[r].m, l, qk_scale);  // row n
-    float inv[4];
+    float l, inv[4];
+    if (lsum) {
+      // row n's sum sits in lane (any column, n >> 2), element n & 3
+      const int i = n & 3;
+      const float mine = i == 0 ? lsum[r][0] : i == 1 ? lsum[r][1] : i == 2 ? lsum[r][2] : lsum[r][3];
+      l = __shfl(mine, 16 * (n >> 2) + n, 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lr = __shfl(l, 4 * c + i, 64);
-      inv[i] = lr > 0.f ? vscale / lr : 0.f;
+      for (int k = 0; k < 4; ++k) inv[k] = lsum[r][k] > 0.f ? vscale / lsum[r][k] : 0.f;
+    } else {
+      l = st[r].l;
+      l += __shfl_xor(l, 16, 64);
+      l += __shfl_xor(l, 32, 64);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lr = __shfl(l, 4 * c + k, 64);
+        inv[k] = lr > 0.f ? vscale / lr : 0.f;
+      }
     }
+    const float lse = row_lse(st[r].m, l, qk_scale);  // row n
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // O rows 4c+i of this lane
       const int R = 4 * c + i;
@@ -256,6 +268,16 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   State<D> st[NT];
 #pragma unroll
   for (int r = 0; r < NT; ++r) state_init(st[r]);
+  // Row sums of the weights in the O layout, accumulated on the matrix cores as P . 1 (one
+  // more product per tile and block) instead of 8 vector adds per tile and block: the
+  // vector ALU, not the matrix cores, is the busier unit here.  They sum the bf16 weights
+  // the P.V product uses.
+  f32x4 lsum[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) lsum[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Frag8 onesf;
+  onesf.q = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 x 8
+  const bf16x8 ones = onesf.v;
 
   const int log2P = a.cache.log2_page, P = 1 << log2P;
   const int64_t tile_b = tile_bytes(KV, P, D);
@@ -320,17 +342,19 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
         }
     }
     float off[NT];
-    softmax_head<D, NT>(st, cur, qk_scale, off, lane);
+    softmax_head<D, NT>(st, cur, qk_scale, off, lane, lsum);
     const char* stg = smem + (i % kPfStages) * SL::BYTES;
     bf16x8 vv[D / 16];
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) vv[dt] = SL::v_operand(stg, dt, lk);
     Frag8 pa[NT];
-    softmax_tail<NT>(st, cur, qk_scale, off, pa);
+    softmax_tail<NT, false>(st, cur, qk_scale, off, pa);
 #pragma unroll
-    for (int r = 0; r < NT; ++r)
+    for (int r = 0; r < NT; ++r) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) st[r].o[dt] = mma(pa[r].v, vv[dt], st[r].o[dt]);
+      lsum[r] = mma(pa[r].v, ones, lsum[r]);  // the weights' row sums: P . 1 (one product per tile)
+    }
 #if PKV_PF_SCHED
     // exponentials and conversions of block i around the scores of block i+1
 #pragma unroll
@@ -359,7 +383,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   }
   if (i < nblk) step(ra, i, sa_, sb_);
   if (!live) return;
-  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane);
+  prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane, lsum);
 }
 
 // Merge of the key splits: one thread per float4 of the output (query row, kv head g,
