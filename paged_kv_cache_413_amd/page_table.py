@@ -43,3 +43,37 @@ def release_out_of_window(block_tables: np.ndarray, context_lens: np.ndarray, ne
     still = np.unique(tables[tables >= 0])
     freed = np.setdiff1d(np.unique(np.array(dropped, dtype=np.int64)), still)
     return tables, freed
+
+
+def shared_pages(block_tables: np.ndarray, context_lens: np.ndarray, page_size: int) -> np.ndarray:
+    """Physical pages that the used part of two or more sequences' tables name: the blocks
+    of a common prefix several requests reuse ("NVIDIA TensorRT-LLM详解：架构、KV Cache、
+    调度与部署实践", §10, cross-request KV reuse)."""
+    used = []
+    for s in range(block_tables.shape[0]):
+        n = -(-int(context_lens[s]) // page_size)
+        used.append(np.unique(block_tables[s, :n]))
+    pages, counts = np.unique(np.concatenate(used) if used else np.zeros(0, np.int32), return_counts=True)
+    return pages[counts > 1]
+
+
+def check_append_targets(block_tables: np.ndarray, context_lens: np.ndarray, new_lens: np.ndarray,
+                         page_size: int, shared=None):
+    """Host-side check before kv_append: no appended row may land in a page other
+    sequences share (a shared prefix page is read by all of them; a request writes only
+    pages of its own, copying a partly matched page first, §11 of the same page), and no two appended rows may
+    name the same (page, slot).  `shared` defaults to shared_pages(...).  Raises
+    ValueError naming the first offending sequence."""
+    if shared is None:
+        shared = shared_pages(block_tables, context_lens, page_size)
+    shared = set(int(p) for p in np.asarray(shared).reshape(-1))
+    seen = {}
+    for s in range(block_tables.shape[0]):
+        L, n = int(context_lens[s]), int(new_lens[s])
+        for t in range(L - n, L):
+            page, slot = int(block_tables[s, t // page_size]), t % page_size
+            if page in shared:
+                raise ValueError(f"sequence {s} appends position {t} into page {page}, which other sequences share")
+            if (page, slot) in seen:
+                raise ValueError(f"sequences {seen[(page, slot)]} and {s} both append into page {page}, slot {slot}")
+            seen[(page, slot)] = s
