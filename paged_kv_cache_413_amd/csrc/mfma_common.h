@@ -29,6 +29,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BT = 32;      // tokens per block
 constexpr int LOG2_BT = 5;
+constexpr int kXcds = 8;    // MI355X: 8 XCDs, each with its own L2; workgroup b runs on XCD b mod 8
 
 // Cache-policy bits of the decode kernels' K/V buffer loads: 2 = non-temporal (the
 // data streams through once per call).  Measured against the default policy: 9-13 %
@@ -603,15 +604,27 @@ __device__ __forceinline__ void mask_v_tail(MxBlock<D>&, int, int) {}
 // four: two lane swaps across 32 and 16 lanes (no LDS permute, no lane arithmetic).
 // The swaps' results are copied out of their vector before the bit casts: a bit cast
 // applied to an element of that vector type reads element 0 whatever the index.
+// max2 is the median of (a, b, +inf): one v_med3 with no quieting of its inputs, which
+// fmaxf needs in IEEE mode for values the compiler cannot prove canonical (lane swaps,
+// matrix-core results).  Scores reaching it are finite or -inf (masked), never NaN.
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __builtin_inff()); }
+
+__device__ __forceinline__ float max8(const float (&x)[8]) {
+  float m = max2(x[0], x[1]);
+#pragma unroll
+  for (int e = 2; e < 8; ++e) m = fmaxf(m, x[e]);
+  return m;
+}
+
 __device__ __forceinline__ float row_max4(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // x[l mod 32] | x[32 + l mod 32]
   const uint32_t a0 = a[0], a1 = a[1];
-  const float y = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
+  const float y = max2(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, a1));
   const uint32_t v = __builtin_bit_cast(uint32_t, y);
   const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);  // rows 2k | 2k+1
   const uint32_t b0 = b[0], b1 = b[1];
-  return fmaxf(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
+  return max2(__builtin_bit_cast(float, b0), __builtin_bit_cast(float, b1));
 }
 
 // Online-softmax update with this block's raw (masked: -inf) scores, then O += P . V.
@@ -664,10 +677,7 @@ template <int D, typename Blk>
 __device__ __forceinline__ void softmax_pv(State<D>& st, const Blk& b, const float (&sc)[8],
                                            float scale, int lane) {
   const int c = lane >> 4;
-  float bm = sc[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[e]);
-  bm = row_max4(bm);
+  const float bm = row_max4(max8(sc));
   const bool grow = (bm - st.m) * scale > kRescaleLog2;  // same in the 4 lanes of a row
   const float mref = grow ? bm : st.m;
   const float off = -mref * scale;
@@ -707,10 +717,7 @@ __device__ __forceinline__ void softmax_head(State<D> (&st)[NT], const float (&s
   bool any = false;
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    float bm = sc[r][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[r][e]);
-    bm = row_max4(bm);
+    const float bm = row_max4(max8(sc[r]));
     grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
     mref[r] = grow[r] ? bm : st[r].m;
     any |= grow[r];
@@ -769,10 +776,7 @@ __device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&
   bool any = false;
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    float bm = sc[r][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, sc[r][e]);
-    bm = row_max4(bm);
+    const float bm = row_max4(max8(sc[r]));
     grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
     mref[r] = grow[r] ? bm : st[r].m;
     any |= grow[r];

@@ -32,7 +32,6 @@ namespace {
 // registers a wave can address and spill.
 template <int D>
 constexpr int kPrefillTiles = D == 128 ? 2 : 4;
-constexpr int kXcds = 8;
 
 // Query tile geometry for G query heads per kv head (per-wave kernel: D's tile count).
 template <int G, int D = 64>
