@@ -8,6 +8,7 @@ instructions are disabled for device code (-packed-fp32-ops).
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,6 +42,53 @@ SOURCE_FLAGS = {
 }
 
 
+# Every source is compiled with the compiler's per-kernel resource report; build() checks
+# it (check_resources) and writes it next to the library (resource_usage.txt).
+REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+RESOURCE_REPORT = os.path.join(PKG, "resource_usage.txt")
+
+
+def parse_resource_remarks(text: str) -> dict:
+    """{kernel name: {field: value}} from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    for ln in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", ln)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z][^:\[]*?)(?: \[[^\]]*\])?: (\S+) \[-Rpass-analysis", ln)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    return out
+
+
+# LDS-shared prefill: three stages of one 32-token block of K and V in bf16 (2 x D x 32
+# x 2 bytes each); any more LDS than that is a register array the compiler moved to
+# LDS (a run-time index into it), which costs a store and a load per use.
+def _prefill_stage_lds(name: str):
+    m = re.search(r"prefill_lds_kernelILi\d+ELi(\d+)ELi\d+E", name)
+    return 3 * 2 * int(m.group(1)) * 32 * 2 if m else None
+
+
+def check_resources(usage: dict) -> list:
+    """Problems in the per-kernel resource report: scratch memory anywhere (no kernel is
+    meant to touch it: registers spilled to memory, or a stack), LDS beyond the prefill
+    stages.  Registers spilled into other registers (SGPRs into vector lanes, VGPRs into
+    AGPRs) cost moves, not memory, and are only reported."""
+    bad = []
+    for name, f in usage.items():
+        if name.startswith("__") or "kernel" not in name:
+            continue
+        if f.get("ScratchSize", "0") != "0":
+            bad.append(f"{name}: scratch {f['ScratchSize']} bytes per lane")
+        if f.get("Dynamic Stack", "False") != "False":
+            bad.append(f"{name}: dynamic stack")
+        lim = _prefill_stage_lds(name)
+        if lim is not None and int(f.get("LDS Size", "0")) > lim:
+            bad.append(f"{name}: LDS {f['LDS Size']} bytes > {lim} of its stages")
+    return bad
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -55,17 +103,26 @@ def sources():
 
 def _compile(hipcc, src):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
+    cmd = [hipcc, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *REMARKS, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    if r.stderr.strip():
-        # hipcc's host pass does not know the packed-fp32 feature; keep other warnings
-        lines = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln
-                 and "not a recognized feature" not in ln]
-        if any(ln.strip() for ln in lines):
-            sys.stderr.write("\n".join(lines) + "\n")
-    return obj
+    usage = parse_resource_remarks(r.stderr)
+    # hipcc's host pass does not know the packed-fp32 feature; keep other warnings (the
+    # resource remarks and their source excerpts go to the report instead)
+    lines, skip = [], False
+    for ln in r.stderr.splitlines():
+        if "remark:" in ln:
+            skip = True
+            continue
+        if skip and (ln.startswith(" ") or not ln.strip()):
+            continue
+        skip = False
+        if "packed-fp32-ops" not in ln and "not a recognized feature" not in ln and ln.strip():
+            lines.append(ln)
+    if lines:
+        sys.stderr.write("\n".join(lines) + "\n")
+    return obj, usage
 
 
 def build(verbose: bool = True) -> str:
@@ -73,7 +130,23 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(hipcc, s), srcs))
+        done = list(ex.map(lambda s: _compile(hipcc, s), srcs))
+    objs = [o for o, _ in done]
+    usage = {}
+    for _, u in done:
+        usage.update(u)
+    with open(RESOURCE_REPORT, "w") as f:
+        f.write("kernel\tVGPRs\tAGPRs\tSGPRs\tSGPR spills (to vector lanes)\tVGPR spills (to AGPRs)\t"
+                "scratch B/lane\tLDS B\twaves/SIMD\n")
+        for name in sorted(usage):
+            u = usage[name]
+            if "kernel" in name and not name.startswith("__"):
+                f.write(f"{name}\t{u.get('VGPRs')}\t{u.get('AGPRs')}\t{u.get('TotalSGPRs')}\t{u.get('SGPRs Spill')}\t"
+                        f"{u.get('VGPRs Spill')}\t"
+                        f"{u.get('ScratchSize')}\t{u.get('LDS Size')}\t{u.get('Occupancy')}\n")
+    bad = check_resources(usage)
+    if bad:
+        raise RuntimeError("kernel resource check failed:\n  " + "\n  ".join(bad))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
