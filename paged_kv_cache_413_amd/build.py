@@ -52,11 +52,13 @@ def parse_resource_remarks(text: str) -> dict:
     """{kernel name: {field: value}} from the compiler's kernel-resource-usage remarks."""
     out, cur = {}, None
     for ln in text.splitlines():
-        m = re.search(r"remark: Function Name: (\S+)", ln)
+        if "remark:" not in ln:
+            continue
+        m = re.search(r"Function Name: (\S+)", ln)
         if m:
             cur = out.setdefault(m.group(1), {})
             continue
-        m = re.search(r"remark:\s+([A-Za-z][^:\[]*?)(?: \[[^\]]*\])?: (\S+) \[-Rpass-analysis", ln)
+        m = re.search(r":\s{2,}([A-Za-z][^:\[]*?)(?: \[[^\]]*\])?: (\S+) \[-Rpass-analysis", ln)
         if m and cur is not None:
             cur[m.group(1).strip()] = m.group(2)
     return out
