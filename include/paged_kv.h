@@ -285,14 +285,16 @@ int paged_kv_debug_gather(const pkv_cache_t* cache, const pkv_seqs_t* seqs, void
  *         operand registers, page ids from a register window of the table; pages of
  *         8 or 16 tokens look each token's page up); 1 = the prefill loaders (a block
  *         fetched by a whole workgroup, decoded and staged in LDS, then read back with
- *         the operand lane map; pages of >= 32 tokens).
+ *         the operand lane map; pages of >= 32 tokens); 2 = the loaders of the dense FP8
+ *         decode kernel (one-query FP8 calls with more (sequence, kv head) pairs than
+ *         resident waves: raw FP8 blocks in flight, widened when folded; pages of >= 32).
  *   k_out, v_out: [num_seqs][max_context_len][num_kv_heads][head_dim] bfloat16: the
  *         values the products use -- bf16 caches as stored, FP8 codes widened exactly
  *         (the per-head scale is applied to the products, not to the operands), MXFP4
  *         elements times their block scale (exact).  Rows t >= context_lens[s] are
  *         left untouched.
- * Caches: BF16 or FP8 with pages of >= 8 tokens (path 1: >= 32), MXFP4 (pages >= 32);
- * PKV_EUNSUPPORTED otherwise. */
+ * Caches: BF16 or FP8 with pages of >= 8 tokens (path 1: >= 32), MXFP4 (pages >= 32),
+ * path 2 FP8 only (pages >= 32); PKV_EUNSUPPORTED otherwise. */
 int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* seqs, int32_t path,
                                    void* k_out, void* v_out, void* stream);
 

@@ -165,6 +165,7 @@ int launch_status(hipError_t e, const char* what) {
 struct DecodePlan {
   bool mfma;       // matrix-core kernels (else the vector-ALU kernel)
   bool auto_mode;  // matrix-core balanced schedule
+  bool dense;      // auto, FP8: the two-waves-per-SIMD kernel (more segments than waves)
   int waves;       // auto: workgroups launched
   int chunk, max_splits;
   size_t off_desc, off_lse, off_o, ws_bytes;
@@ -179,10 +180,11 @@ constexpr int kMinShareBlocks = 4;  // auto schedule: at least 4 x 32 tokens per
 // the calls the setting thread makes, and nothing but that explicit call sets it.
 thread_local int g_auto_waves_override = 0;
 
-// Waves of the balanced schedule: the device's resident count, or the test override.
-int auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
+// Waves of the balanced schedule: the device's resident count of the chosen kernel, or
+// the test override.
+int auto_waves(int kv_dtype, int head_dim, int group, int page_size, bool dense = false) {
   if (g_auto_waves_override > 0) return g_auto_waves_override;
-  return std::max(1, pkv::mfma_auto_waves(kv_dtype, head_dim, group, page_size));
+  return std::max(1, pkv::mfma_auto_waves(kv_dtype, head_dim, group, page_size, dense));
 }
 
 // Device validation of a call before its kernels, when PKV_DEBUG=1 is set in the
@@ -219,6 +221,12 @@ DecodePlan plan_decode(const pkv::CacheArgs& c, const pkv::SeqArgs& s, int num_q
   if (p.mfma && num_splits == 0) {
     p.auto_mode = true;
     p.waves = auto_waves(c.dtype, c.head_dim, G, P);
+    // One query per sequence, FP8, pages of >= 32 tokens: more (sequence, kv head)
+    // segments than waves take the dense kernel (its own resident count)
+    if (record_rows == 0 && c.dtype == pkv::DT_FP8 && P >= 32 && int64_t(s.num_seqs) * c.num_kv_heads > p.waves) {
+      p.dense = true;
+      p.waves = auto_waves(c.dtype, c.head_dim, G, P, true);
+    }
     p.chunk = 0;
     p.max_splits = 0;
     const size_t recs = size_t(2) * p.waves;  // up to two cut segments per wave
@@ -427,7 +435,7 @@ int paged_attn_decode(const pkv_cache_t* cache, const pkv_seqs_t* seqs, const vo
     a.num_waves = p.waves;
     a.min_share = kMinShareBlocks;
     a.ws_desc = p.auto_mode ? reinterpret_cast<int4*>(ws + p.off_desc) : nullptr;
-    pkv::MfmaPlan mp{p.auto_mode, p.waves, false};
+    pkv::MfmaPlan mp{p.auto_mode, p.waves, false, p.dense};
     return launch_status(pkv::launch_mfma_decode(a, mp, hs), "paged_attn_decode");
   }
   return launch_status(pkv::launch_valu_decode(a, hs), "paged_attn_decode");
@@ -488,7 +496,7 @@ int paged_attn_prefill_chunk(const pkv_cache_t* cache, const pkv_seqs_t* seqs, c
     a.ws_desc = reinterpret_cast<int4*>(ws + p.dec.off_desc);
     a.num_waves = p.dec.waves;
     a.min_share = kMinShareBlocks;
-    pkv::MfmaPlan mp{true, p.dec.waves, true};
+    pkv::MfmaPlan mp{true, p.dec.waves, true, false};
     return launch_status(pkv::launch_mfma_decode(a, mp, hs), "paged_attn_prefill_chunk");
   }
   if (p.mfma) {
@@ -529,7 +537,8 @@ int paged_kv_debug_gather_operands(const pkv_cache_t* cache, const pkv_seqs_t* s
   int st;
   if ((st = check_cache(cache, c)) != PKV_OK) return st;
   if ((st = check_seqs(seqs, c, s)) != PKV_OK) return st;
-  if (path != 0 && path != 1) return fail(PKV_EINVAL, "path must be 0 (decode loaders) or 1 (prefill loaders)");
+  if (path < 0 || path > 2)
+    return fail(PKV_EINVAL, "path must be 0 (decode loaders), 1 (prefill loaders) or 2 (dense FP8 decode loaders)");
   if (!pkv::operands_supported(c.dtype, c.page_size, c.head_dim, path))
     return fail(PKV_EUNSUPPORTED, "no matrix-core loader for cache dtype %d, page size %d, path %d", c.dtype,
                 c.page_size, path);

@@ -50,11 +50,15 @@ struct RowKeys {
 
 // Fold one block into the state of the tile's rows.  On the blocks that reach a row's
 // limit or start before a row's window the excluded keys' scores are masked, and on the
-// range's last, partial block the V entries past t_end are zeroed.  An MXFP4 block is
-// decoded first (ready); a bf16 / FP8 one is used as loaded.
+// range's last, partial block the V entries past t_end are zeroed.  An MXFP4 or raw FP8
+// block is decoded first (ready); a bf16 / widened FP8 one is used as loaded.
 template <int D, typename Blk>
 __device__ __forceinline__ void fold_block(State<D>& st, Blk& b, const bf16x8 (&qf)[D / 32],
                                            float qk_scale, int t, const RowKeys& k, int lane) {
+  constexpr bool kRaw = std::is_same_v<Blk, F8Block<D>>;  // its tail is masked on the codes
+  if constexpr (kRaw) {
+    if (t + BT > k.t_end) mask_v_tail<D>(b, k.t_end - t, lane);
+  }
   const auto& r = ready<D>(b);
   float sc[8];
   block_scores<D>(r, qf, sc);
@@ -65,18 +69,20 @@ __device__ __forceinline__ void fold_block(State<D>& st, Blk& b, const bf16x8 (&
       const int tk = t + tok_of(c, e);
       if (tk >= lim || tk < k.lo_row) sc[e] = -INFINITY;
     }
-    if (t + BT > k.t_end) mask_v_tail<D>(b, k.t_end - t, lane);
+    if constexpr (!kRaw) {
+      if (t + BT > k.t_end) mask_v_tail<D>(b, k.t_end - t, lane);
+    }
   }
   softmax_pv<D>(st, r, sc, qk_scale, lane);
 }
 
 // Blocks [b0, b1) of one (sequence, kv head).
-template <int KV, int D, bool SMALLP>
+template <int KV, int D, bool SMALLP, bool RAW = false>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                           int b0, int b1, const RowKeys& k, int L, int log2P,
                                           int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  run_blocks<KV, D, SMALLP>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](auto& b, int t) {
+  run_blocks<KV, D, SMALLP, RAW>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](auto& b, int t) {
     fold_block<D>(st, b, qf, qk_scale, t, k, lane);
   });
 }
@@ -147,6 +153,16 @@ constexpr int kWgWaves = PKV_DECODE_WG_WAVES;
 #endif
 template <int KV>
 constexpr int kDecodeWavesPerEu = KV == DT_MXFP4 ? PKV_MX_WAVES_PER_EU : PKV_DECODE_WAVES_PER_EU;
+
+// Dense FP8 decode (DENSE): raw FP8 blocks, widened when folded (half the registers of a
+// widened block), and two waves per SIMD.  The host picks it for one-query FP8 calls with
+// more (sequence, kv head) segments than one wave per SIMD gives waves: each wave then
+// starts several segments, and every start is a chain of dependent loads (lengths, table
+// window, first block) that a second wave on the SIMD covers.  Measured on the mixed
+// batch's FP8 decode (2 048 segments): 185 -> 171 us; on 512 - 1 024 segments (Llama-shaped
+// FP8 batches, the shared-prefix batch) it is 3 - 10 % slower, so those keep one wave.
+template <int KV, bool DENSE>
+constexpr int kAutoWavesPerEu = DENSE ? 2 : kDecodeWavesPerEu<KV>;
 
 // ---- fixed partitions: one wave per (sequence, kv head, partition) ---------------------
 template <int KV, int D, int G, bool SMALLP>
@@ -245,8 +261,9 @@ __device__ __forceinline__ void locate(const int32_t* __restrict__ lens, const i
 // tile's rows are (query, head) pairs, query j of sequence s is packed row
 // cu_q_lens[s] + j at position L - nq + j, and records hold 16 rows.  Otherwise one
 // query per sequence (packed row s) and records of G rows.
-template <int KV, int D, int G, bool SMALLP, bool MQ>
-__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kDecodeWavesPerEu<KV>, kDecodeWavesPerEu<KV>))) void decode_auto_kernel(AttnArgs a) {
+template <int KV, int D, int G, bool SMALLP, bool MQ, bool DENSE = false>
+__global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(kAutoWavesPerEu<KV, DENSE>, kAutoWavesPerEu<KV, DENSE>))) void decode_auto_kernel(AttnArgs a) {
+  static_assert(!DENSE || (KV == DT_FP8 && !SMALLP && !MQ), "dense decode: one-query FP8 calls, pages >= 32");
   if (halted(a.cache)) return;
   constexpr int ROWS = MQ ? 16 : G;
   const int lane = threadIdx.x & 63;
@@ -309,7 +326,7 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
     const int t_end = min(L, (blo + b1) << LOG2_BT);
     const int pos = L - nq + (lane & 15) / G;  // position of this lane's row's query
     const RowKeys k{t_end, pos + 1, min(t_end, L - nq + 1), window_lo(pos, W), window_lo(L - 1, W)};
-    run_range<KV, D, SMALLP>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, blo + b0,
+    run_range<KV, D, SMALLP, DENSE>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, blo + b0,
                              blo + b1, k, L, a.cache.log2_page, Hkv * tile_b, g * tile_b, lane);
     const bool complete = b0 == 0 && b1 == nb;
     finish<D, G, ROWS>(st, a, q0, nq, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
@@ -377,7 +394,15 @@ hipError_t launch_t(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
       }
       return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP, false>), grid, block, 0, st, a);
+    if constexpr (KV == DT_FP8 && !SMALLP) {
+      if (p.dense)
+        hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, false, false, true>), grid, block, 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, false, false>), grid, block, 0, st, a);
+    } else {
+      if (p.dense) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((decode_auto_kernel<KV, D, G, SMALLP, false>), grid, block, 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((merge_auto_kernel<D, G, false>), dim3(p.waves), dim3(kAutoMergeThreads), 0, st, a);
@@ -422,10 +447,12 @@ hipError_t dispatch_d(const AttnArgs& a, const MfmaPlan& p, hipStream_t st) {
 // Kernel whose occupancy sizes the auto grid (one instance per head_dim / dtype is
 // representative: G only changes which MFMA rows are used).
 template <int KV, int D>
-const void* auto_kernel_for(int G, bool smallp) {
+const void* auto_kernel_for(int G, bool smallp, bool dense) {
   // (MXFP4 has no short-page kernels: its instance stands in for both)
-#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, KV != DT_MXFP4, false>) \
-                          : reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, false, false>))
+#define PKV_K(GG) (smallp ? reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, KV != DT_MXFP4, false>)   \
+                   : dense && KV == DT_FP8                                                                       \
+                       ? reinterpret_cast<const void*>(&decode_auto_kernel<DT_FP8, D, GG, false, false, true>)   \
+                       : reinterpret_cast<const void*>(&decode_auto_kernel<KV, D, GG, false, false>))
   switch (G) {
     case 1: return PKV_K(1);
     case 2: return PKV_K(2);
@@ -445,16 +472,17 @@ bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, i
          page_size >= (kv_dtype == DT_MXFP4 ? BT : 8);
 }
 
-int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size) {
+int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size, bool dense) {
   const bool smallp = page_size < BT;
+  dense = dense && kv_dtype == DT_FP8 && !smallp;
   const void* k = kv_dtype == DT_BF16
-                      ? (head_dim == 64 ? auto_kernel_for<DT_BF16, 64>(group, smallp)
-                                        : auto_kernel_for<DT_BF16, 128>(group, smallp))
+                      ? (head_dim == 64 ? auto_kernel_for<DT_BF16, 64>(group, smallp, false)
+                                        : auto_kernel_for<DT_BF16, 128>(group, smallp, false))
                   : kv_dtype == DT_FP8
-                      ? (head_dim == 64 ? auto_kernel_for<DT_FP8, 64>(group, smallp)
-                                        : auto_kernel_for<DT_FP8, 128>(group, smallp))
-                      : (head_dim == 64 ? auto_kernel_for<DT_MXFP4, 64>(group, false)
-                                        : auto_kernel_for<DT_MXFP4, 128>(group, false));
+                      ? (head_dim == 64 ? auto_kernel_for<DT_FP8, 64>(group, smallp, dense)
+                                        : auto_kernel_for<DT_FP8, 128>(group, smallp, dense))
+                      : (head_dim == 64 ? auto_kernel_for<DT_MXFP4, 64>(group, false, false)
+                                        : auto_kernel_for<DT_MXFP4, 128>(group, false, false));
   return resident_blocks(k, 64 * kWgWaves) * kWgWaves;
 }
 

@@ -6,7 +6,8 @@
 //
 // Path 0 runs the decode kernels' block pipeline (run_blocks: the page window held in a
 // register, per-tile buffer descriptors, blocks in flight) and writes each block as its
-// registers hold it.  Path 1 runs the prefill kernel's staging (Stager: a workgroup
+// registers hold it; path 2 the same pipeline with the dense FP8 decode kernel's raw
+// blocks (widened when folded).  Path 1 runs the prefill kernel's staging (Stager: a workgroup
 // fetches a block, decodes it to bf16 into LDS) and reads the operands back from the
 // stage with the prefill kernel's lane map.  Values: bf16 caches as stored, FP8 codes
 // widened exactly, MXFP4 elements times their block scale.
@@ -38,7 +39,7 @@ __device__ __forceinline__ void write_v8(uint16_t* out, int64_t row0, int Hkv, i
   }
 }
 
-template <int KV, int D, bool SMALLP>
+template <int KV, int D, bool SMALLP, bool RAW = false>
 __global__ __launch_bounds__(64) void operands_decode_kernel(CacheArgs c, SeqArgs sq, uint16_t* __restrict__ k_out,
                                                              uint16_t* __restrict__ v_out) {
   if (halted(c)) return;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(64) void operands_decode_kernel(CacheArgs c, SeqArg
   const int64_t row0 = int64_t(s) * sq.max_context_len;  // row (s, t) of the outputs, kv head added below
   uint16_t* ko = k_out + int64_t(g) * D;
   uint16_t* vo = v_out + int64_t(g) * D;
-  run_blocks<KV, D, SMALLP>(static_cast<const char*>(c.pool), bt, 0, (L + BT - 1) >> LOG2_BT, L, c.log2_page,
+  run_blocks<KV, D, SMALLP, RAW>(static_cast<const char*>(c.pool), bt, 0, (L + BT - 1) >> LOG2_BT, L, c.log2_page,
                             Hkv * tile_b, g * tile_b, lane, [&](auto& blk, int t) {
     const auto& r = ready<D>(blk);
 #pragma unroll
@@ -123,6 +124,8 @@ hipError_t launch_d(const CacheArgs& c, const SeqArgs& s, int path, uint16_t* k,
   const dim3 grid(unsigned(int64_t(s.num_seqs) * c.num_kv_heads));
   if (path == 1) {
     if constexpr (KV != DT_F32) hipLaunchKernelGGL((operands_prefill_kernel<KV, D>), grid, dim3(kPfThreads), 0, st, c, s, k, v);
+  } else if (path == 2) {
+    if constexpr (KV == DT_FP8) hipLaunchKernelGGL((operands_decode_kernel<KV, D, false, true>), grid, dim3(64), 0, st, c, s, k, v);
   } else if (c.page_size >= BT) {
     hipLaunchKernelGGL((operands_decode_kernel<KV, D, false>), grid, dim3(64), 0, st, c, s, k, v);
   } else {
@@ -140,6 +143,7 @@ hipError_t launch_k(const CacheArgs& c, const SeqArgs& s, int path, uint16_t* k,
 
 bool operands_supported(int kv_dtype, int page_size, int head_dim, int path) {
   if (head_dim != 64 && head_dim != 128) return false;
+  if (path == 2) return kv_dtype == DT_FP8 && page_size >= BT;
   if (kv_dtype == DT_MXFP4 || path == 1) return page_size >= BT && kv_dtype != DT_F32;
   return (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && page_size >= 8;
 }

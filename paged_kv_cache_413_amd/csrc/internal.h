@@ -79,9 +79,10 @@ struct MfmaPlan {
   int waves;
   bool multi_query;  // auto only: several queries per sequence (prefill chunks of at most
                      // 16 / G queries, packed by cu_q_lens), 16-row partial records
+  bool dense;        // auto, one query, FP8, pages >= 32: the two-waves-per-SIMD kernel
 };
 bool mfma_decode_supported(int kv_dtype, int q_dtype, int head_dim, int group, int page_size);
-int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size);
+int mfma_auto_waves(int kv_dtype, int head_dim, int group, int page_size, bool dense = false);
 hipError_t launch_mfma_decode(const AttnArgs& a, const MfmaPlan& p, hipStream_t stream);
 
 // Matrix-core prefill kernels (prefill_mfma.hip): same support as the decode kernels.

@@ -296,8 +296,60 @@ struct MxBlock {
   uint32_t vs[D / 16];
 };
 
-template <int KV, int D>
-using BlockOf = std::conditional_t<KV == DT_MXFP4, MxBlock<D>, Block<D>>;
+// ---- raw FP8 blocks ------------------------------------------------------------------------
+// One 32-token block of an FP8 tile (pages of >= 32 tokens) as loaded: the E4M3 codes of
+// the lane's operands (8 per uint2, in the lane layout of Block), widened to bf16 only
+// when the block is folded (ready).  Half the registers of a widened block: the dense
+// decode kernel runs two waves per SIMD with these.
+template <int D>
+struct F8Block {
+  uint2 ka[D / 32], kb[D / 32];
+  uint2 v[D / 16];
+};
+
+// RAW: FP8 blocks stay raw in the pipeline (F8Block) instead of being widened on load.
+template <int KV, int D, bool RAW = false>
+using BlockOf = std::conditional_t<KV == DT_MXFP4, MxBlock<D>,
+                                   std::conditional_t<RAW && KV == DT_FP8, F8Block<D>, Block<D>>>;
+
+__device__ __forceinline__ uint2 bload_raw8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, PKV_KV_LOAD_AUX));
+  return make_uint2(w[0], w[1]);
+}
+
+// The loads of load_block<DT_FP8, D, false>, without the widening.
+template <int D>
+__device__ __forceinline__ void load_block_f8(F8Block<D>& b, const char* __restrict__ pool, const PageWindow& win,
+                                              int t, int log2P, int64_t kv_stride_b, int64_t head_off_b,
+                                              LaneOffsets lo) {
+  const int P = 1 << log2P;
+  const int32_t page = page_of(win, t >> log2P);
+  const uint32_t slot0 = uint32_t(t & (P - 1));
+  const uint32_t tile_bytes = uint32_t(P) * D;
+  const char* K = uniform_ptr(pool + int64_t(page) * 2 * kv_stride_b + head_off_b);
+  const auto rk = tile_rsrc(K, tile_bytes);
+  const auto rv = tile_rsrc(K + kv_stride_b, tile_bytes);
+  const uint32_t ks = slot0 * 32, vs = slot0 * D;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const uint32_t kj = __builtin_amdgcn_readfirstlane(ks + uint32_t(j * 32) * P);
+    b.ka[j] = bload_raw8(rk, lo.k, kj);
+    b.kb[j] = bload_raw8(rk, lo.k + 16 * 32, kj);
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    b.v[dt] = bload_raw8(rv, lo.v, __builtin_amdgcn_readfirstlane(vs + uint32_t(16 * BT * dt)));
+}
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint2 w) {
+  Frag8 f;
+  f.w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false));
+  f.w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true));
+  f.w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false));
+  f.w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true));
+  return f.v;
+}
 
 // `n` bytes (4, 8, 16 or 32) at voff + soff of a tile, as words.
 template <int N>
@@ -381,6 +433,19 @@ struct MxReady {
 
 template <int D>
 __device__ __forceinline__ const Block<D>& ready(const Block<D>& b) { return b; }
+
+template <int D>
+__device__ __forceinline__ Block<D> ready(const F8Block<D>& b) {
+  Block<D> r;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    r.ka[j] = fp8x8_to_bf16(b.ka[j]);
+    r.kb[j] = fp8x8_to_bf16(b.kb[j]);
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = fp8x8_to_bf16(b.v[dt]);
+  return r;
+}
 
 template <int D>
 __device__ __forceinline__ MxReady<D> ready(const MxBlock<D>& b) {
@@ -592,6 +657,21 @@ __device__ __forceinline__ void mask_v_tail(Block<D>& b, int nvalid, int lane) {
       f.w[w] &= keep;
     }
     b.v[dt] = f.v;
+  }
+}
+
+// Raw FP8 blocks: the same zeroing on the codes (code 0 widens to +0).
+template <int D>
+__device__ __forceinline__ void mask_v_tail(F8Block<D>& b, int nvalid, int lane) {
+  const int c = lane >> 4;
+  uint32_t keep[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (tok_of(c, e) < nvalid) keep[e >> 2] |= 0xffu << (8 * (e & 3));
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    b.v[dt].x &= keep[0];
+    b.v[dt].y &= keep[1];
   }
 }
 
@@ -819,19 +899,22 @@ __device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&
 // prefetches all lie in the range and are unconditional, so each fold waits only for
 // its own block's loads (a partial vmcnt), never for later prefetches; the last blocks
 // take a tail whose prefetches are guarded.
-template <int KV, int D, bool SMALLP, typename FoldFn>
+template <int KV, int D, bool SMALLP, bool RAW, typename FoldFn>
 __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                                 const PageWindow& win, int b0, int b1, int L, int log2P,
                                                 int64_t kv_stride_b, int64_t head_off_b, int lane, FoldFn& fold) {
+  static_assert(!RAW || (KV == DT_FP8 && !SMALLP), "raw blocks: FP8 caches with pages of >= 32 tokens");
   constexpr int N = KV == DT_MXFP4 ? PKV_MX_DEPTH : PKV_DECODE_DEPTH;
   const LaneOffsets lo = lane_offsets<KV, D>(lane);
-  auto ld = [&](BlockOf<KV, D>& b, int blk) {
+  auto ld = [&](BlockOf<KV, D, RAW>& b, int blk) {
     if constexpr (KV == DT_MXFP4)
       load_block_mx<D>(b, pool, win, blk << LOG2_BT, log2P, kv_stride_b, head_off_b, lane);
+    else if constexpr (RAW)
+      load_block_f8<D>(b, pool, win, blk << LOG2_BT, log2P, kv_stride_b, head_off_b, lo);
     else
       load_block<KV, D, SMALLP>(b, pool, bt, win, blk << LOG2_BT, L, log2P, kv_stride_b, head_off_b, lo, lane);
   };
-  BlockOf<KV, D> buf[N];
+  BlockOf<KV, D, RAW> buf[N];
   const int nb = b1 - b0;
   int i = 0;
   if (nb >= 2 * N - 1) {
@@ -863,13 +946,13 @@ __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, c
 // window, then pipelines its blocks with no table load inside the loop (a conditional
 // load there would make every iteration wait for all loads in flight, prefetches
 // included).  The pipeline drains once per 64 pages.
-template <int KV, int D, bool SMALLP, typename FoldFn>
+template <int KV, int D, bool SMALLP, bool RAW = false, typename FoldFn>
 __device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                            int b0, int b1, int L, int log2P, int64_t kv_stride_b,
                                            int64_t head_off_b, int lane, FoldFn fold) {
   if constexpr (SMALLP) {
     const PageWindow none{0, 0};
-    pipeline_blocks<KV, D, true>(pool, bt, none, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, fold);
+    pipeline_blocks<KV, D, true, RAW>(pool, bt, none, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, fold);
   } else {
     const int log2bp = log2P - LOG2_BT;  // blocks per page, log2
     const int npages = (L + (1 << log2P) - 1) >> log2P;
@@ -878,7 +961,7 @@ __device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const 
       const int c1 = min(b1, (base + 64) << log2bp);
       PageWindow win;
       load_window(win, bt, base, npages, lane);
-      pipeline_blocks<KV, D, false>(pool, bt, win, c0, c1, L, log2P, kv_stride_b, head_off_b, lane, fold);
+      pipeline_blocks<KV, D, false, RAW>(pool, bt, win, c0, c1, L, log2P, kv_stride_b, head_off_b, lane, fold);
       c0 = c1;
     }
   }

@@ -2,7 +2,8 @@
 
 paged_kv_debug_gather_operands runs the matrix-core kernels' page loaders over every
 cached token -- path 0 the decode block pipeline (page window in a register, buffer
-descriptors, blocks in flight; per-token table lookups on pages of 8 and 16), path 1
+descriptors, blocks in flight; per-token table lookups on pages of 8 and 16), path 2
+the same pipeline with the dense FP8 decode kernel's raw blocks, path 1
 the prefill kernel's LDS staging (a workgroup fetches and decodes each block, the waves
 read it back with their operand lane map) -- and writes the K and V operands back in
 logical order.  They must equal, bit for bit, the oracle's plain gather (page =
@@ -49,8 +50,10 @@ def _expected(wl, pool, s, L, g):
 
 
 # path 1 (the prefill staging) serves pages of >= 32 tokens; shorter pages prefill
-# through the decode loaders of path 0
-PATH_CASES = [(kv, P, D, path) for (kv, P, D) in CASES for path in (0, 1) if path == 0 or P >= 32]
+# through the decode loaders of path 0; path 2 (the dense FP8 decode kernel's raw blocks)
+# serves FP8 caches with pages of >= 32 tokens
+PATH_CASES = [(kv, P, D, path) for (kv, P, D) in CASES for path in (0, 1, 2)
+              if (path == 0 or P >= 32) and (path != 2 or kv == "fp8")]
 
 
 @pytest.mark.parametrize("kv,P,D,path", PATH_CASES, ids=lambda x: str(x))
@@ -119,3 +122,13 @@ def test_operands_reject_unsupported_caches(gpu_lib):
     with pytest.raises(B.PagedKVError) as e:
         B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, 0, k, k)
     assert e.value.code == B.PKV_EUNSUPPORTED
+    # path 2 (dense FP8 decode loaders) serves FP8 caches only; path 3 does not exist
+    wl = workloads.make(2, num_seqs=2, len_range=(40, 90))   # bf16, pages of 64
+    db = DeviceBatch(wl)
+    db.prepare_step()
+    with pytest.raises(B.PagedKVError) as e:
+        B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, 2, k, k)
+    assert e.value.code == B.PKV_EUNSUPPORTED
+    with pytest.raises(B.PagedKVError) as e:
+        B.paged_kv_debug_gather_operands(db.cache, db.seqs_all, 3, k, k)
+    assert e.value.code == B.PKV_EINVAL

@@ -252,6 +252,32 @@ def test_many_short_sequences(gpu_lib, kv, num_seqs, splits):
     assert_lse_close(lse, ref[1], kv, f"S={num_seqs}")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_dense_fp8_decode_past_one_wave_per_segment(gpu_lib, kv):
+    """One-query FP8 calls with more (sequence, kv head) segments than one wave per SIMD
+    gives waves run the dense kernel (raw FP8 blocks, two waves per SIMD: twice the waves,
+    so a larger workspace); fewer segments, or bf16 caches, keep the one-wave kernel.
+    Both match the oracle."""
+    from tests.device_batch import DeviceBatch
+    sizes = {}
+    for S in (100, 200):                       # 800 and 1 600 segments of 8 kv heads
+        wl = workloads.make(2, num_seqs=S, len_range=(1, 200), kv_dtype=kv, num_splits=0)
+        print(f"[case] dense decode kv={kv} S={S}", flush=True)
+        db = DeviceBatch(wl)
+        db.fill_history()
+        db.step()
+        torch.cuda.synchronize()
+        dec, lse, _, _ = db.outputs_f64()
+        ref = oracle_outputs(wl, oracle_pool(wl))
+        assert_close(dec, ref[0], kv, f"S={S}")
+        assert_lse_close(lse, ref[1], kv, f"S={S}")
+        sizes[S] = db.ws_dec_bytes
+    if kv == "fp8":
+        assert sizes[200] > 1.5 * sizes[100], sizes     # twice the waves, twice the records
+    else:
+        assert sizes[200] == sizes[100], sizes          # same resident waves either way
+
+
 AUTO_WAVES = [
     # (waves, workload, overrides): few waves, so shares are long and spread over
     # several (sequence, kv head) segments, and segments over several waves
@@ -263,7 +289,8 @@ AUTO_WAVES = [
                  head_dim=64)),                                    # G = 8, pages of 16
     (40, 2, dict(lens=[1, 31, 32, 33, 95, 300, 4000], page_size=8, num_q_heads=128,
                  num_kv_heads=8, head_dim=128)),                   # G = 16, pages of 8
-    (20, 5, dict(num_seqs=6, group_size=3, prefix_len=128, len_range=(129, 600))),  # fp8 KV
+    (20, 5, dict(num_seqs=6, group_size=3, prefix_len=128, len_range=(129, 600))),  # fp8 KV, 48 segments: dense
+    (30, 5, dict(num_seqs=3, group_size=3, prefix_len=128, len_range=(129, 900))),  # fp8 KV, 24 segments: one wave/SIMD
     (1, 2, dict(lens=[1, 700, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
                 head_dim=128)),                                    # one wave does it all
 ]
