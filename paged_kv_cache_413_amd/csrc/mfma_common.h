@@ -783,6 +783,33 @@ __device__ __forceinline__ void softmax_pv(State<D>& st, const Blk& b, const flo
   pv_product<D>(st.o, p, b);
 }
 
+// row_max4 of NT tiles' rows, each step issued for every tile before the next step: the
+// tiles' dependent chains (eight-value maximum, two lane swaps, two maxima) interleave
+// instead of running one after the other.
+template <int NT>
+__device__ __forceinline__ void row_max4_n(const float (&sc)[NT][8], float (&out)[NT]) {
+  uint32_t u[NT], a0[NT], a1[NT];
+#pragma unroll
+  for (int r = 0; r < NT; ++r) u[r] = __builtin_bit_cast(uint32_t, max8(sc[r]));
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const auto a = __builtin_amdgcn_permlane32_swap(u[r], u[r], false, false);
+    a0[r] = a[0];
+    a1[r] = a[1];
+  }
+#pragma unroll
+  for (int r = 0; r < NT; ++r)
+    u[r] = __builtin_bit_cast(uint32_t, max2(__builtin_bit_cast(float, a0[r]), __builtin_bit_cast(float, a1[r])));
+#pragma unroll
+  for (int r = 0; r < NT; ++r) {
+    const auto b = __builtin_amdgcn_permlane16_swap(u[r], u[r], false, false);
+    a0[r] = b[0];
+    a1[r] = b[1];
+  }
+#pragma unroll
+  for (int r = 0; r < NT; ++r) out[r] = max2(__builtin_bit_cast(float, a0[r]), __builtin_bit_cast(float, a1[r]));
+}
+
 // The same update split in two for NT tiles of 16 rows that share one block, so that
 // the caller can put other work (the next block's scores) between and around them.
 // softmax_head: the maxima, the vote and the rare rescale of l and O (a branch);
@@ -795,9 +822,11 @@ __device__ __forceinline__ void softmax_head(State<D> (&st)[NT], const float (&s
   bool grow[NT];
   float mref[NT];
   bool any = false;
+  float bms[NT];
+  row_max4_n<NT>(sc, bms);
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    const float bm = row_max4(max8(sc[r]));
+    const float bm = bms[r];
     grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
     mref[r] = grow[r] ? bm : st[r].m;
     any |= grow[r];
@@ -854,9 +883,11 @@ __device__ __forceinline__ void softmax_tiles(State<D> (&st)[NT], const float (&
   bool grow[NT];
   float mref[NT];
   bool any = false;
+  float bms[NT];
+  row_max4_n<NT>(sc, bms);
 #pragma unroll
   for (int r = 0; r < NT; ++r) {
-    const float bm = row_max4(max8(sc[r]));
+    const float bm = bms[r];
     grow[r] = (bm - st[r].m) * scale > kRescaleLog2;
     mref[r] = grow[r] ? bm : st[r].m;
     any |= grow[r];
