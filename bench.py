@@ -185,6 +185,30 @@ def memory_report(wl) -> dict:
             "saving": round(1.0 - unique / static, 4)}
 
 
+def device_report() -> dict:
+    """The GPU as the runtime reports it (the peaks above are AMD's published figures for
+    MI355X; these fields confirm the part they are applied to)."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    out = {"name": p.name, "compute_units": p.multi_processor_count, "memory_bytes": int(p.total_memory)}
+    for k in ("gcnArchName", "L2_cache_size", "warp_size", "max_threads_per_multi_processor"):
+        v = getattr(p, k, None)
+        if v is not None:
+            out[k] = v if isinstance(v, (int, float)) else str(v)
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def stream_read(nbytes: int, reps: int):
     """The library's plain streaming read of nbytes (the decode launch shape), reps times
     back to back between two HIP events on the launch stream: GB/s."""
@@ -280,7 +304,7 @@ def cpu_baseline(wl, budget_s: float):
             if t_spent >= budget_s:
                 break
     gbs = bytes_done / t_spent / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"{seqs_sampled} of {len(order)} {'chunk' if prefill_only else 'decode'} sequences of "
                        f"{wl.name}, {calls} timed sequence calls ({bytes_done / 1e6:.1f} MB of KV, "
                        f"{t_spent:.1f} s): kv_append of the step's tokens then fp64 "
@@ -503,6 +527,7 @@ def main():
                    "context_tokens": int(wl.context_lens.sum()), "num_splits": ns, "window": wl.window,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens / (ms_step * 1e-3), 1),
+        "tokens_per_s_cold_median": round(tokens / (float(np.median(step_cold)) * 1e-6), 1),
         "hbm_frac_step": round(kv_gbs / HBM_PEAK_GBS, 4),
         "kv_bytes": ab["kv"],
         "kernel_us": {"kv_append": round(append_us, 2),
@@ -521,6 +546,7 @@ def main():
         "stream_read": sr,
         "memory": memory_report(wl),
         "kernel_source_hash": {k: kernel_source_hash(k) for k in KERNEL_SOURCES},
+        "device": device_report(),
     }
     if shared:
         lg = ab["total"] / (call_us * 1e-6) / 1e9
