@@ -291,6 +291,8 @@ AUTO_WAVES = [
                  num_kv_heads=8, head_dim=128)),                   # G = 16, pages of 8
     (20, 5, dict(num_seqs=6, group_size=3, prefix_len=128, len_range=(129, 600))),  # fp8 KV, 48 segments: dense
     (30, 5, dict(num_seqs=3, group_size=3, prefix_len=128, len_range=(129, 900))),  # fp8 KV, 24 segments: one wave/SIMD
+    (12, 2, dict(lens=[1, 63, 700, 2100, 33, 300], page_size=128, num_q_heads=16, num_kv_heads=4,
+                 head_dim=64, kv_dtype="fp8")),                    # fp8, D = 64, pages of 128: dense
     (1, 2, dict(lens=[1, 700, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
                 head_dim=128)),                                    # one wave does it all
 ]
@@ -458,6 +460,7 @@ WINDOWS = [
     (2, dict(num_seqs=7, len_range=(1, 700), num_splits=3), 64),                   # fixed partitions
     (2, dict(lens=[5, 40, 333, 1000], page_size=16, num_q_heads=16, num_kv_heads=2, head_dim=64), 77),
     (5, dict(num_seqs=6, group_size=3, prefix_len=128, len_range=(129, 600)), 200),  # FP8, shared prefix
+    (2, dict(num_seqs=140, len_range=(1, 300), kv_dtype="fp8"), 100),             # FP8, 1 120 segments: dense decode
     (1, dict(), 20),                                                               # f32: vector-ALU kernels
     (3, dict(num_seqs=9, num_prefill=2, prefill_chunk=70, prefill_cached=190, median=60, clip=(1, 400)), 50),
     (3, dict(num_seqs=0, num_prefill=5, prefill_chunk=[4, 1, 3, 4, 2],
