@@ -27,7 +27,9 @@
 //
 // Schedule: "auto" spreads the flattened (sequence, kv head, block) space evenly over
 // the resident waves (each wave a contiguous run of blocks, possibly spanning several
-// sequences); a range that covers a whole (sequence, kv head) writes the output
+// sequences; each XCD takes a contiguous eighth of that order; FP8 calls with more
+// segments than waves use the two-waves-per-SIMD "dense" variant with raw FP8 blocks);
+// a range that covers a whole (sequence, kv head) writes the output
 // directly, a cut one writes a normalised partial and its log-sum-exp, and a small
 // merge kernel combines the pieces exactly (log-sum-exp weights).  "fixed" gives each
 // page-aligned partition of a fixed size its own wave, as in a conventional split-KV
