@@ -56,7 +56,7 @@ typedef enum {
 typedef enum {
   PKV_OK = 0,
   PKV_EINVAL = -1,        /* a null pointer, a bad size or an inconsistent argument */
-  PKV_EUNSUPPORTED = -2,  /* a valid combination this build has no kernel for */
+  PKV_EUNSUPPORTED = -2,  /* a valid combination the library has no kernel for */
   PKV_EWORKSPACE = -3,    /* workspace missing or smaller than the size function says */
   PKV_ELAUNCH = -4        /* the HIP runtime refused the launch */
 } pkv_status_t;
