@@ -293,6 +293,12 @@ AUTO_WAVES = [
     (30, 5, dict(num_seqs=3, group_size=3, prefix_len=128, len_range=(129, 900))),  # fp8 KV, 24 segments: one wave/SIMD
     (12, 2, dict(lens=[1, 63, 700, 2100, 33, 300], page_size=128, num_q_heads=16, num_kv_heads=4,
                  head_dim=64, kv_dtype="fp8")),                    # fp8, D = 64, pages of 128: dense
+    (8, 2, dict(lens=[1, 95, 700, 1500, 33], page_size=64, num_q_heads=128, num_kv_heads=8,
+                head_dim=128, kv_dtype="fp8")),                    # fp8 dense, G = 16
+    (6, 2, dict(lens=[31, 64, 650, 1200, 2], page_size=32, num_q_heads=8, num_kv_heads=8,
+                head_dim=64, kv_dtype="fp8")),                     # fp8 dense, G = 1, pages of 32
+    (10, 2, dict(lens=[3, 300, 901, 47], page_size=64, num_q_heads=16, num_kv_heads=8,
+                 head_dim=128, kv_dtype="fp8")),                   # fp8 dense, G = 2
     (1, 2, dict(lens=[1, 700, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
                 head_dim=128)),                                    # one wave does it all
 ]
