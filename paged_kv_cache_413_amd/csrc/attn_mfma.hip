@@ -297,48 +297,84 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   int64_t cum;
   locate(lens, cu, W, S, Hkv, f0, lane, s, cum);
   const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
-  int64_t f = f0;
-  bool first = true;
-  while (f < fend) {
-    const int L = uniform32(lens[s]);
-    const int q0 = MQ ? uniform32(a.cu_q_lens[s]) : s;
-    const int nq = MQ ? uniform32(a.cu_q_lens[s + 1]) - q0 : 1;
-    int blo;
-    const int nb = seg_blocks(L, nq, W, blo);
-    const int64_t seg0 = Hkv * cum;
-    const int g = int((f - seg0) / nb);
-    const int64_t gs = seg0 + int64_t(g) * nb;            // this segment's first flat block
-    const int b0 = int(f - gs);
-    const int b1 = int(min(int64_t(nb), fend - gs));
+  // The piece of this wave's share in segment (s, g) that holds flat block f: its
+  // sequence geometry, and the flat block gs where the segment starts.
+  struct Piece {
+    int L, q0, nq, blo, nb, g;
+    int64_t gs;
+  };
+  auto piece_of = [&](int s_, int64_t cum_, int64_t f_) {
+    Piece pc;
+    pc.L = uniform32(lens[s_]);
+    pc.q0 = MQ ? uniform32(a.cu_q_lens[s_]) : s_;
+    pc.nq = MQ ? uniform32(a.cu_q_lens[s_ + 1]) - pc.q0 : 1;
+    pc.nb = seg_blocks(pc.L, pc.nq, W, pc.blo);
+    const int64_t seg0 = Hkv * cum_;
+    pc.g = int((f_ - seg0) / pc.nb);
+    pc.gs = seg0 + int64_t(pc.g) * pc.nb;
+    return pc;
+  };
+  // Fold the piece of segment (s, g) from flat block f to the segment's end or fend.
+  // `first`: the piece at f0 (the share's first, record slot 0, described to the merge).
+  auto run_piece = [&](int s_, const Piece& pc, int64_t f_, bool first) {
+    const int b0 = int(f_ - pc.gs);
+    const int b1 = int(min(int64_t(pc.nb), fend - pc.gs));
     if (first && lane == 0) {
       // This wave merges its first segment when that segment started in an earlier
       // wave (w0) and ends inside this one.  Record slot of w0: 1 unless the segment
       // is w0's first too.
-      const int64_t w0 = gs / share;
-      const bool merges = gs < f0 && gs + nb <= fend;
-      *desc = make_int4(s, g, int(w0), merges ? (1 | (gs != w0 * share ? 2 : 0)) : 0);
+      const int64_t w0 = pc.gs / share;
+      const bool merges = pc.gs < f0 && pc.gs + pc.nb <= fend;
+      *desc = make_int4(s_, pc.g, int(w0), merges ? (1 | (pc.gs != w0 * share ? 2 : 0)) : 0);
     }
     float qk_scale, vscale;
-    scales<KV>(a, g, qk_scale, vscale);
+    scales<KV>(a, pc.g, qk_scale, vscale);
     bf16x8 qf[D / 32];
-    load_q<D, G>(qf, a.q, q0, nq, a.num_q_heads, g, lane);
+    load_q<D, G>(qf, a.q, pc.q0, pc.nq, a.num_q_heads, pc.g, lane);
     State<D> st;
     state_init(st);
-    const int32_t* bt = a.seqs.block_tables + int64_t(s) * a.seqs.max_pages_per_seq;
-    const int t_end = min(L, (blo + b1) << LOG2_BT);
+    const int32_t* bt = a.seqs.block_tables + int64_t(s_) * a.seqs.max_pages_per_seq;
+    const int L = pc.L, nq = pc.nq;
+    const int t_end = min(L, (pc.blo + b1) << LOG2_BT);
     const int pos = L - nq + (lane & 15) / G;  // position of this lane's row's query
     const RowKeys k{t_end, pos + 1, min(t_end, L - nq + 1), window_lo(pos, W), window_lo(L - 1, W)};
-    run_range<KV, D, SMALLP, DENSE>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, blo + b0,
-                             blo + b1, k, L, a.cache.log2_page, Hkv * tile_b, g * tile_b, lane);
-    const bool complete = b0 == 0 && b1 == nb;
-    finish<D, G, ROWS>(st, a, q0, nq, g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale, lane);
+    run_range<KV, D, SMALLP, DENSE>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, pc.blo + b0,
+                                    pc.blo + b1, k, L, a.cache.log2_page, Hkv * tile_b, pc.g * tile_b, lane);
+    const bool complete = b0 == 0 && b1 == pc.nb;
+    finish<D, G, ROWS>(st, a, pc.q0, nq, pc.g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale,
+                       lane);
+    return pc.gs + b1;
+  };
+  // Order of the pieces: a share whose first piece continues a segment begun in an
+  // earlier wave folds that piece last, so every wave starts at the head of a segment.
+  // The heads of neighbouring requests' segments are where a shared prefix lies: the
+  // waves that read the same prefix pages then read them at about the same time, and
+  // one L2 fetch serves several of them.  Each piece is computed exactly as in flat
+  // order (same blocks, same record slots), so the results do not change.
+  const int s_first = s;
+  const int64_t cum_first = cum;
+  const Piece p_first = piece_of(s, cum, f0);
+  const bool defer = f0 > p_first.gs && p_first.gs + p_first.nb < fend;
+  int64_t f = f0;
+  bool first = true;
+  if (defer) {
+    f = p_first.gs + p_first.nb;
+    if (p_first.g + 1 == Hkv) {
+      cum += p_first.nb;
+      ++s;
+    }
     first = false;
-    f = gs + b1;
-    if (g + 1 == Hkv) {
-      cum += nb;
+  }
+  while (f < fend) {
+    const Piece pc = piece_of(s, cum, f);
+    f = run_piece(s, pc, f, first);
+    first = false;
+    if (pc.g + 1 == Hkv) {
+      cum += pc.nb;
       ++s;
     }
   }
+  if (defer) run_piece(s_first, p_first, f0, true);
 }
 
 // Merge of one cut (sequence, kv head) segment of the balanced schedule, by the
