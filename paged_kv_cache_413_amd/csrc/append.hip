@@ -18,14 +18,45 @@
 namespace pkv {
 namespace {
 
-// Sequence that owns packed row `row`: the largest s with cu[s] <= row.
+// Sequence that owns packed row `row`: the largest s with cu[s] <= row.  cu is
+// non-decreasing from cu[0] = 0, so that is the number of s in 1 .. num_seqs-1 with
+// cu[s] <= row.  The lanes of a wave test 256 entries per round, all loads issued
+// before any count: one memory round trip per round where a binary search takes
+// log2(num_seqs) dependent ones.  The result is the same in every lane.
 __device__ __forceinline__ int owner_of(const int32_t* __restrict__ cu, int num_seqs, int row) {
-  int lo = 0, hi = num_seqs;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= row) lo = mid; else hi = mid;
+  const int lane = threadIdx.x & 63;
+  int cnt = 0;
+  for (int b = 1; b < num_seqs; b += 256) {
+    int v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = cu[min(b + 64 * k + lane, num_seqs - 1)];  // unconditional loads
+    bool le[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) le[k] = b + 64 * k + lane < num_seqs && v[k] <= row;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cnt += __popcll(__ballot(le[k]));
   }
-  return lo;
+  return __builtin_amdgcn_readfirstlane(cnt);
+}
+
+// The 16 (bf16 or fp8 caches: bf16 in) or 32 (f32) input bytes one thread of the
+// append moves.
+template <int IN>
+struct AppendSrc {
+  uint4 w[IN == DT_F32 ? 2 : 1];
+};
+
+template <int IN>
+__device__ __forceinline__ AppendSrc<IN> append_src(const void* __restrict__ in, int64_t elem) {
+  AppendSrc<IN> r;
+  if constexpr (IN == DT_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(in) + elem);
+    r.w[0] = p[0];
+    r.w[1] = p[1];
+  } else {
+    r.w[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + elem);
+  }
+  return r;
 }
 
 template <int IN, int KV>
@@ -35,41 +66,53 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
                                                         const int32_t* __restrict__ cu) {
   if (halted(c)) return;
   const int row = blockIdx.x;
-  const int s = owner_of(cu, sq.num_seqs, row);
-  const int n = cu[s + 1] - cu[s];
-  const int pos = sq.context_lens[s] - n + (row - cu[s]);
-  const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
   const int D = c.head_dim, H = c.num_kv_heads;
   const int vec_per_head = D / 8;
   const int vec_per_row = H * vec_per_head;
   const int log2P = c.log2_page;
-  for (int i = threadIdx.x; i < 2 * vec_per_row; i += blockDim.x) {
-    const int kv = i >= vec_per_row;
+  // Input element of item i; the first item's bytes are loaded before the slot lookup
+  // (they depend on the row alone), so their latency overlaps its dependent loads.
+  auto src_of = [&](int i, int& kv, int& h, int& e0) {
+    kv = i >= vec_per_row;
     const int j = i - kv * vec_per_row;
-    const int h = j / vec_per_head;
-    const int e0 = (j - h * vec_per_head) * 8;
-    const int64_t src = (int64_t(row) * H + h) * D + e0;
-    const void* in = kv ? v_new : k_new;
+    h = j / vec_per_head;
+    e0 = (j - h * vec_per_head) * 8;
+    return (int64_t(row) * H + h) * D + e0;
+  };
+  const int i0 = threadIdx.x;
+  AppendSrc<IN> first{};
+  if (i0 < 2 * vec_per_row) {
+    int kv, h, e0;
+    const int64_t src = src_of(i0, kv, h, e0);
+    first = append_src<IN>(kv ? v_new : k_new, src);
+  }
+  const int s = owner_of(cu, sq.num_seqs, row);
+  const int n = cu[s + 1] - cu[s];
+  const int pos = sq.context_lens[s] - n + (row - cu[s]);
+  const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
+  for (int i = i0; i < 2 * vec_per_row; i += blockDim.x) {
+    int kv, h, e0;
+    const int64_t src = src_of(i, kv, h, e0);
+    const AppendSrc<IN> in = i == i0 ? first : append_src<IN>(kv ? v_new : k_new, src);
     // K rows are contiguous in the tile (one vector store); V is dim-major inside its
     // sub-block, so the eight elements go to eight consecutive dims, one sub-block
     // length apart.
     const int64_t dst = elem_offset(bt, pos, log2P, kv, h, H, D, e0);
     const int64_t step = kv ? (int64_t(1) << v_sub_log2(log2P)) : 1;
     if constexpr (KV == DT_F32) {
-      const float4* s4 = reinterpret_cast<const float4*>(static_cast<const float*>(in) + src);
       float* pool = static_cast<float*>(c.pool);
       if (!kv) {
-        float4* d4 = reinterpret_cast<float4*>(pool + dst);
-        d4[0] = s4[0];
-        d4[1] = s4[1];
+        uint4* d4 = reinterpret_cast<uint4*>(pool + dst);
+        d4[0] = in.w[0];
+        d4[1] = in.w[1];
       } else {
-        const float4 a = s4[0], b = s4[1];
-        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint4 a = in.w[0], b = in.w[1];
+        const uint32_t x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pool[dst + e * step] = x[e];
+        for (int e = 0; e < 8; ++e) pool[dst + e * step] = __uint_as_float(x[e]);
       }
     } else if constexpr (KV == DT_BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + src);
+      const uint4 w = in.w[0];
       uint16_t* pool = static_cast<uint16_t*>(c.pool);
       if (!kv) {
         *reinterpret_cast<uint4*>(pool + dst) = w;
@@ -79,7 +122,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(CacheArgs c, SeqArgs sq,
         for (int e = 0; e < 8; ++e) pool[dst + e * step] = uint16_t(ws[e >> 1] >> ((e & 1) * 16));
       }
     } else {  // bf16 in, E4M3 out
-      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(in) + src);
+      const uint4 w = in.w[0];
       const float inv = (kv ? c.v_inv_scale : c.k_inv_scale)[h];
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
       uint32_t code[8];
@@ -128,17 +171,28 @@ __device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, float a, float b, floa
   }
 }
 
-// 32 consecutive bf16 values at `src` (64-byte aligned).  The scale byte is max(E - 2,
+// 32 consecutive bf16 values (load32: 64-byte aligned).  The scale byte is max(E - 2,
 // 0), E the bf16 exponent field of the largest magnitude (floor(log2) of a normal value
 // is E - 127; a zero or subnormal maximum takes the clamp, byte 0 = 2^-127); each
 // element is then x / 2^(byte - 127) rounded onto the E2M1 grid (e2m1_pair).  The
 // scale passed to the conversion is the float whose exponent field is the byte (for
 // byte 0 that is +0.0, whose exponent field 0 the conversion reads as 2^-127).
-__device__ __forceinline__ MxCodes mx_encode32(const uint16_t* __restrict__ src) {
+struct Bf16x32 {
+  uint4 v[4];
+};
+
+__device__ __forceinline__ Bf16x32 load32(const uint16_t* __restrict__ src) {
+  Bf16x32 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.v[i] = reinterpret_cast<const uint4*>(src)[i];
+  return r;
+}
+
+__device__ __forceinline__ MxCodes mx_encode32(const Bf16x32& x) {
   uint32_t h[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+    const uint4 v = x.v[i];
     h[4 * i] = v.x;
     h[4 * i + 1] = v.y;
     h[4 * i + 2] = v.z;
@@ -176,24 +230,33 @@ __global__ __launch_bounds__(64) void kv_append_mx_kernel(CacheArgs c, SeqArgs s
                                                           const int32_t* __restrict__ cu) {
   if (halted(c)) return;
   const int row = blockIdx.x;
+  const int D = c.head_dim, H = c.num_kv_heads, P = c.page_size, J = D / 32;
+  // The row's own K or V block of the first item, loaded before the slot lookup (it
+  // depends on the row alone) so that its latency overlaps the lookup's loads.
+  const int i0 = threadIdx.x;
+  Bf16x32 own{};
+  if (i0 < 2 * H * J) {
+    const int kv = i0 >= H * J;
+    const int hj = i0 - kv * H * J;
+    own = load32((kv ? v_new : k_new) + int64_t(row) * H * D + hj * 32);
+  }
   const int s = owner_of(cu, sq.num_seqs, row);
   const int first = cu[s], n = cu[s + 1] - first;
   const int L = sq.context_lens[s], pos0 = L - n;
   const int pos = pos0 + (row - first);
   const int32_t* bt = sq.block_tables + int64_t(s) * sq.max_pages_per_seq;
-  const int D = c.head_dim, H = c.num_kv_heads, P = c.page_size, J = D / 32;
   const int64_t tb = tile_bytes(DT_MXFP4, P, D);
   uint8_t* pool = static_cast<uint8_t*>(c.pool);
   const int32_t page = bt[pos >> c.log2_page];
   const int slot = pos & (P - 1);
   const bool v_owner = !(pos & 1) || pos - 1 < pos0;
-  for (int i = threadIdx.x; i < 2 * H * J; i += blockDim.x) {
+  for (int i = i0; i < 2 * H * J; i += blockDim.x) {
     const int kv = i >= H * J;
     const int hj = i - kv * H * J;
     const int h = hj / J, j = hj - (hj / J) * J;
     uint8_t* tile = pool + ((int64_t(page) * 2 + kv) * H + h) * tb;
     if (!kv) {
-      const MxCodes e = mx_encode32(k_new + (int64_t(row) * H + h) * D + 32 * j);
+      const MxCodes e = mx_encode32(i == i0 ? own : load32(k_new + (int64_t(row) * H + h) * D + 32 * j));
 #pragma unroll
       for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(tile + mx_k_word(slot, 32 * j + 8 * q, D)) = e.w[q];
       tile[mx_k_scale(P, slot, j, D)] = uint8_t(e.scale);
@@ -206,19 +269,26 @@ __global__ __launch_bounds__(64) void kv_append_mx_kernel(CacheArgs c, SeqArgs s
         const int p = pb + u;
         fresh[u] = p >= pos0 && p < L;
         if (fresh[u]) {
-          e[u] = mx_encode32(v_new + (int64_t(first + p - pos0) * H + h) * D + 32 * j);
+          e[u] = mx_encode32(p == pos && i == i0 ? own
+                                                 : load32(v_new + (int64_t(first + p - pos0) * H + h) * D + 32 * j));
           tile[mx_v_scale(P, sl + u, j, D)] = uint8_t(e[u].scale);
         } else {
           e[u] = MxCodes{{0u, 0u, 0u, 0u}, 0u};
         }
       }
       const uint32_t keep = (fresh[0] ? 0u : 0x0fu) | (fresh[1] ? 0u : 0xf0u);
+      // The 32 bytes are distinct (one per dim): every old byte is read before any is
+      // written, so the reads are in flight together rather than one per round trip.
+      uint32_t old[32] = {};
+      if (keep) {
+#pragma unroll
+        for (int d = 0; d < 32; ++d) old[d] = tile[mx_v_byte(sl, 32 * j + d, D)];
+      }
+#pragma unroll
       for (int d = 0; d < 32; ++d) {
-        uint8_t* byte = tile + mx_v_byte(sl, 32 * j + d, D);  // low nibble: slot sl, high: sl + 1
-        const uint32_t lo = (e[0].w[d >> 3] >> (4 * (d & 7))) & 15u;
+        const uint32_t lo = (e[0].w[d >> 3] >> (4 * (d & 7))) & 15u;  // low nibble: slot sl, high: sl + 1
         const uint32_t hi = (e[1].w[d >> 3] >> (4 * (d & 7))) & 15u;
-        const uint32_t old = keep ? uint32_t(*byte) : 0u;
-        *byte = uint8_t((old & keep) | ((lo | (hi << 4)) & ~keep));
+        tile[mx_v_byte(sl, 32 * j + d, D)] = uint8_t((old[d] & keep) | ((lo | (hi << 4)) & ~keep));
       }
     }
   }
