@@ -523,10 +523,13 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 32], const void* __restr
 // R / G of the sequence, head g*G + R % G; rows of queries >= nq are skipped) x D.
 // One workgroup of NT threads: every thread owns float4 chunks of the record (one row
 // each) and a stride of records, and keeps a running (max, sum of weights, weighted
-// sum) over them, so the loads of different records are independent and in flight
-// together; the record-parallel states are then combined in LDS.  Every thread of the
-// workgroup must call it (it may hold barriers); it may be called repeatedly.
+// sum) over them.  It loads its records kMergeBatch at a time, every load of a batch
+// issued before any is used (the loads past the last record repeat it and are not
+// used), so a batch costs one memory round trip; the record-parallel states are then
+// combined in LDS.  Every thread of the workgroup must call it (it may hold barriers);
+// it may be called repeatedly.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 4;
 
 template <int D, int G, int ROWS, int NT, typename RecFn>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int q0, int nq, int g, int n, RecFn rec) {
@@ -544,22 +547,34 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int q0, int nq
     m[k] = -INFINITY;
     w[k] = 0.f;
   }
-#pragma unroll 4
-  for (int i = rp; i < n; i += RP) {
-    const int64_t r = rec(i);
+  constexpr int KB = kMergeBatch;
+  for (int i0 = rp; i0 < n; i0 += KB * RP) {
+    float x[KB][CPT];
+    float4 o[KB][CPT];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) {
-      const int e = (cl + k * CC) * 4;
-      if (e < ROWS * D && (e / D) / G < nq) {
-        const float x = a.ws_lse[r * ROWS + e / D];
-        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + r * (ROWS * D) + e);
-        if (x == -INFINITY) continue;  // a piece that saw no key of this row
-        const float mn = fmaxf(m[k], x);
-        const float sa = __expf(m[k] - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
-        acc[k].x = acc[k].x * sa + o.x * sb;
-        acc[k].y = acc[k].y * sa + o.y * sb;
-        acc[k].z = acc[k].z * sa + o.z * sb;
-        acc[k].w = acc[k].w * sa + o.w * sb;
+    for (int u = 0; u < KB; ++u) {
+      const int64_t r = rec(min(i0 + u * RP, n - 1));
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int e = min((cl + k * CC) * 4, ROWS * D - 4);  // chunks past the record: unused
+        x[u][k] = a.ws_lse[r * ROWS + e / D];
+        o[u][k] = *reinterpret_cast<const float4*>(a.ws_o + r * (ROWS * D) + e);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (i0 + u * RP >= n) break;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int e = (cl + k * CC) * 4;
+        // rows of queries past the sequence's, and pieces that saw no key of the row
+        if (e >= ROWS * D || (e / D) / G >= nq || x[u][k] == -INFINITY) continue;
+        const float mn = fmaxf(m[k], x[u][k]);
+        const float sa = __expf(m[k] - mn), sb = __expf(x[u][k] - mn);  // m = -inf: sa = 0
+        acc[k].x = acc[k].x * sa + o[u][k].x * sb;
+        acc[k].y = acc[k].y * sa + o[u][k].y * sb;
+        acc[k].z = acc[k].z * sa + o[u][k].z * sb;
+        acc[k].w = acc[k].w * sa + o[u][k].w * sb;
         w[k] = w[k] * sa + sb;
         m[k] = mn;
       }

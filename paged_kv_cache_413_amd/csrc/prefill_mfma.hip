@@ -405,19 +405,31 @@ __global__ __launch_bounds__(kPfMergeThreads) void prefill_merge_kernel(AttnArgs
   const int e = ch * 4, h = e / D, d = e % D;
   float m = -INFINITY, w = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i = 0; i < nsplit; ++i) {
-    const int64_t rec = rg * nsplit + i;
-    const float x = a.ws_lse[rec * G + h];
-    const float4 o = *reinterpret_cast<const float4*>(a.ws_o + rec * (G * D) + e);
-    if (x == -INFINITY) continue;
-    const float mn = fmaxf(m, x);
-    const float sa = __expf(m - mn), sb = __expf(x - mn);  // m = -inf: sa = 0
-    acc.x = acc.x * sa + o.x * sb;
-    acc.y = acc.y * sa + o.y * sb;
-    acc.z = acc.z * sa + o.z * sb;
-    acc.w = acc.w * sa + o.w * sb;
-    w = w * sa + sb;
-    m = mn;
+  // kMergeBatch splits per round, every load of a round issued before any is used
+  // (loads past the last split repeat it and are not used): one memory round trip each.
+  constexpr int KB = kMergeBatch;
+  for (int i0 = 0; i0 < nsplit; i0 += KB) {
+    float x[KB];
+    float4 o[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int64_t rec = rg * nsplit + min(i0 + u, nsplit - 1);
+      x[u] = a.ws_lse[rec * G + h];
+      o[u] = *reinterpret_cast<const float4*>(a.ws_o + rec * (G * D) + e);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (i0 + u >= nsplit) break;
+      if (x[u] == -INFINITY) continue;
+      const float mn = fmaxf(m, x[u]);
+      const float sa = __expf(m - mn), sb = __expf(x[u] - mn);  // m = -inf: sa = 0
+      acc.x = acc.x * sa + o[u].x * sb;
+      acc.y = acc.y * sa + o[u].y * sb;
+      acc.z = acc.z * sa + o[u].z * sb;
+      acc.w = acc.w * sa + o[u].w * sb;
+      w = w * sa + sb;
+      m = mn;
+    }
   }
   const float inv = 1.f / w;
   uint16_t* out = static_cast<uint16_t*>(a.out) + (row * a.num_q_heads + g * G + h) * D + d;
