@@ -72,11 +72,16 @@ def _prefill_stage_lds(name: str):
     return 3 * 2 * int(m.group(1)) * 32 * 2 if m else None
 
 
+# Kernels that use no LDS by design (the decode kernels hold everything in registers):
+# any LDS in them is a register array the compiler moved there (a run-time index).
+NO_LDS = ("decode_auto_kernel", "decode_fixed_kernel")
+
+
 def check_resources(usage: dict) -> list:
     """Problems in the per-kernel resource report: scratch memory anywhere (no kernel is
     meant to touch it: registers spilled to memory, or a stack), LDS beyond the prefill
-    stages.  Registers spilled into other registers (SGPRs into vector lanes, VGPRs into
-    AGPRs) cost moves, not memory, and are only reported."""
+    stages, LDS in the decode kernels.  Registers spilled into other registers (SGPRs
+    into vector lanes, VGPRs into AGPRs) cost moves, not memory, and are only reported."""
     bad = []
     for name, f in usage.items():
         if name.startswith("__") or "kernel" not in name:
@@ -88,6 +93,8 @@ def check_resources(usage: dict) -> list:
         lim = _prefill_stage_lds(name)
         if lim is not None and int(f.get("LDS Size", "0")) > lim:
             bad.append(f"{name}: LDS {f['LDS Size']} bytes > {lim} of its stages")
+        if any(k in name for k in NO_LDS) and int(f.get("LDS Size", "0")) > 0:
+            bad.append(f"{name}: LDS {f['LDS Size']} bytes in a kernel that uses none")
     return bad
 
 

@@ -79,14 +79,16 @@ __device__ __forceinline__ void fold_block(State<D>& st, Blk& b, const bf16x8 (&
 }
 
 // Blocks [b0, b1) of one (sequence, kv head).
+// win0: the block-table window of block b0's page, already loaded (or NULL).
 template <int KV, int D, bool SMALLP, bool RAW = false>
 __device__ __forceinline__ void run_range(State<D>& st, const bf16x8 (&qf)[D / 32], float qk_scale,
                                           const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                           int b0, int b1, const RowKeys& k, int L, int log2P,
-                                          int64_t kv_stride_b, int64_t head_off_b, int lane) {
-  run_blocks<KV, D, SMALLP, RAW>(pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, [&](auto& b, int t) {
-    fold_block<D>(st, b, qf, qk_scale, t, k, lane);
-  });
+                                          int64_t kv_stride_b, int64_t head_off_b, int lane,
+                                          const PageWindow* win0 = nullptr) {
+  run_blocks<KV, D, SMALLP, RAW>(
+      pool, bt, b0, b1, L, log2P, kv_stride_b, head_off_b, lane,
+      [&](auto& b, int t) { fold_block<D>(st, b, qf, qk_scale, t, k, lane); }, win0);
 }
 
 // Finish a range: reduce the running sum over the four lane groups of each row and
@@ -226,22 +228,146 @@ __device__ __forceinline__ int queries_of(const int32_t* __restrict__ cu, int s)
   return cu ? cu[s + 1] - cu[s] : 1;
 }
 
-// Total blocks of all (sequence, kv head) segments.
-__device__ __forceinline__ int64_t total_blocks(const int32_t* __restrict__ lens, const int32_t* __restrict__ cu,
-                                                int W, int S, int Hkv, int lane) {
-  int64_t sum = 0;
-  int blo;
-  for (int s = lane; s < S; s += 64) sum += seg_blocks(lens[s], queries_of(cu, s), W, blo);
+// Value v of lane l (l wave-uniform), in scalar registers.
+__device__ __forceinline__ int64_t lane64(int64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(uint64_t(v)), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(uint64_t(v) >> 32), l);
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// Lengths (and, with several queries per sequence, the first packed row and the query
+// count) of the first kSeqCache sequences, one per lane and 64-sequence chunk, with the
+// inclusive running sum of their segment blocks.  A wave loads them once, every load
+// issued before any is used; the share's location and each later segment's geometry
+// then come from registers (readlane) instead of a chain of dependent loads.  Sequences
+// past them are read from memory.
+constexpr int kSeqChunks = 4;
+constexpr int kSeqCache = 64 * kSeqChunks;
+
+template <bool MQ>
+struct SeqCache {
+  int L[kSeqChunks];
+  int q0[MQ ? kSeqChunks : 1], nq[MQ ? kSeqChunks : 1];
+  int64_t incl[kSeqChunks];  // segment blocks (per kv head) of sequences 0 .. 64k + lane
+  int64_t run;               // ... of all cached sequences
+  int n;                     // cached sequences: min(S, kSeqCache)
+};
+
+// Entry s (< kSeqCache, wave-uniform) of a cached array: lane s mod 64 of chunk s / 64.
+// Every chunk is read with a constant index (a run-time index into the array would
+// put the cache in scratch memory).
+__device__ __forceinline__ int cached(const int (&v)[kSeqChunks], int s) {
+  const int l = s & 63, k = s >> 6;
+  int r = __builtin_amdgcn_readlane(v[0], l);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  return uniform64(sum * Hkv);
+  for (int j = 1; j < kSeqChunks; ++j) {
+    const int x = __builtin_amdgcn_readlane(v[j], l);
+    r = k == j ? x : r;
+  }
+  return r;
+}
+
+template <bool MQ>
+__device__ __forceinline__ void load_seqs(SeqCache<MQ>& c, const int32_t* __restrict__ lens,
+                                          const int32_t* __restrict__ cu, int W, int S, int lane) {
+  c.n = min(S, kSeqCache);
+#pragma unroll
+  for (int k = 0; k < kSeqChunks; ++k) {
+    const int s = min(64 * k + lane, S - 1);  // unconditional loads; lanes past S unused
+    c.L[k] = lens[s];
+    if constexpr (MQ) {
+      c.q0[k] = cu[s];
+      c.nq[k] = cu[s + 1];
+    }
+  }
+  int64_t run = 0;
+#pragma unroll
+  for (int k = 0; k < kSeqChunks; ++k) {
+    if constexpr (MQ) c.nq[k] -= c.q0[k];
+    if (64 * k < c.n) {  // wave-uniform
+      int blo;
+      const int64_t nb = 64 * k + lane < c.n ? int64_t(seg_blocks(c.L[k], MQ ? c.nq[k] : 1, W, blo)) : 0;
+      c.incl[k] = run + wave_incl_scan(nb, lane);
+      run = lane64(c.incl[k], 63);
+    } else {
+      c.incl[k] = run;
+    }
+  }
+  c.run = run;
+}
+
+// Length, first packed row and query count of sequence s (wave-uniform).
+template <bool MQ>
+__device__ __forceinline__ void seq_info(const SeqCache<MQ>& c, const int32_t* __restrict__ lens,
+                                         const int32_t* __restrict__ cu, int s, int& L, int& q0, int& nq) {
+  if (s < c.n) {
+    L = cached(c.L, s);
+    if constexpr (MQ) {
+      q0 = cached(c.q0, s);
+      nq = cached(c.nq, s);
+    }
+  } else {
+    L = uniform32(lens[s]);
+    if constexpr (MQ) {
+      q0 = uniform32(cu[s]);
+      nq = uniform32(cu[s + 1]) - q0;
+    }
+  }
+  if constexpr (!MQ) {
+    q0 = s;
+    nq = 1;
+  }
+}
+
+// Total blocks of all (sequence, kv head) segments.
+template <bool MQ>
+__device__ __forceinline__ int64_t total_blocks(const SeqCache<MQ>& c, const int32_t* __restrict__ lens,
+                                                const int32_t* __restrict__ cu, int W, int S, int Hkv,
+                                                int lane) {
+  int64_t sum = 0;
+  if (S > kSeqCache) {  // wave-uniform
+    int blo;
+    for (int s = kSeqCache + lane; s < S; s += 64) sum += seg_blocks(lens[s], queries_of(cu, s), W, blo);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  }
+  return uniform64((c.run + sum) * Hkv);
 }
 
 // Sequence whose segments contain flat block f, and its cum (blocks before it).
-__device__ __forceinline__ void locate(const int32_t* __restrict__ lens, const int32_t* __restrict__ cu, int W,
-                                       int S, int Hkv, int64_t f, int lane, int& s_out, int64_t& cum_out) {
-  int64_t run = 0;
-  for (int base = 0; base < S; base += 64) {
+template <bool MQ>
+__device__ __forceinline__ void locate(const SeqCache<MQ>& c, const int32_t* __restrict__ lens,
+                                       const int32_t* __restrict__ cu, int W, int S, int Hkv, int64_t f,
+                                       int lane, int& s_out, int64_t& cum_out) {
+  if (f < Hkv * c.run) {
+    // first chunk k with a sequence whose segments reach past f, and that sequence's
+    // lane; every chunk is read with a constant index (a run-time one would put the
+    // cache in memory)
+    int k = 0;
+    uint64_t hit = 0;
+#pragma unroll
+    for (int j = kSeqChunks - 1; j >= 0; --j) {
+      const uint64_t h = __ballot(64 * j + lane < c.n && Hkv * c.incl[j] > f);
+      if (h) {
+        k = j;
+        hit = h;
+      }
+    }
+    const int first = __builtin_ctzll(hit);
+    int64_t incl = lane64(c.incl[0], first);
+#pragma unroll
+    for (int j = 1; j < kSeqChunks; ++j) {
+      const int64_t x = lane64(c.incl[j], first);
+      incl = k == j ? x : incl;
+    }
+    int L, q0, nq, blo;
+    s_out = 64 * k + first;
+    seq_info(c, lens, cu, s_out, L, q0, nq);
+    cum_out = incl - seg_blocks(L, nq, W, blo);
+    return;
+  }
+  int64_t run = c.run;
+  for (int base = kSeqCache; base < S; base += 64) {
     const int s = base + lane;
     int blo;
     const int64_t nb = s < S ? int64_t(seg_blocks(lens[s], queries_of(cu, s), W, blo)) : 0;
@@ -284,7 +410,9 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   const int32_t* lens = a.seqs.context_lens;
   const int32_t* cu = MQ ? a.cu_q_lens : nullptr;
   const int W = a.seqs.window;
-  const int64_t T = total_blocks(lens, cu, W, S, Hkv, lane);
+  SeqCache<MQ> sc;
+  load_seqs(sc, lens, cu, W, S, lane);
+  const int64_t T = total_blocks(sc, lens, cu, W, S, Hkv, lane);
   const int64_t share = max(int64_t(a.min_share), (T + a.num_waves - 1) / a.num_waves);
   const int64_t f0 = int64_t(w) * share;
   int4* desc = a.ws_desc + w;
@@ -295,8 +423,9 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   const int64_t fend = min(T, f0 + share);
   int s;
   int64_t cum;
-  locate(lens, cu, W, S, Hkv, f0, lane, s, cum);
+  locate(sc, lens, cu, W, S, Hkv, f0, lane, s, cum);
   const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
+  const int log2P = a.cache.log2_page;
   // The piece of this wave's share in segment (s, g) that holds flat block f: its
   // sequence geometry, and the flat block gs where the segment starts.
   struct Piece {
@@ -305,18 +434,28 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   };
   auto piece_of = [&](int s_, int64_t cum_, int64_t f_) {
     Piece pc;
-    pc.L = uniform32(lens[s_]);
-    pc.q0 = MQ ? uniform32(a.cu_q_lens[s_]) : s_;
-    pc.nq = MQ ? uniform32(a.cu_q_lens[s_ + 1]) - pc.q0 : 1;
+    seq_info(sc, lens, cu, s_, pc.L, pc.q0, pc.nq);
     pc.nb = seg_blocks(pc.L, pc.nq, W, pc.blo);
     const int64_t seg0 = Hkv * cum_;
     pc.g = int((f_ - seg0) / pc.nb);
     pc.gs = seg0 + int64_t(pc.g) * pc.nb;
     return pc;
   };
+  // Block-table window of the piece's first page (pages of >= 32 tokens), loaded one
+  // piece ahead: a wave that moves to its next segment then waits only for that
+  // segment's first blocks, not for the table entries in front of them.
+  auto window_of = [&](int s_, const Piece& pc, int64_t f_) {
+    PageWindow win{0, 0};
+    if constexpr (!SMALLP) {
+      const int first_blk = pc.blo + int(f_ - pc.gs);
+      load_window(win, a.seqs.block_tables + int64_t(s_) * a.seqs.max_pages_per_seq,
+                  first_blk >> (log2P - LOG2_BT), (pc.L + (1 << log2P) - 1) >> log2P, lane);
+    }
+    return win;
+  };
   // Fold the piece of segment (s, g) from flat block f to the segment's end or fend.
   // `first`: the piece at f0 (the share's first, record slot 0, described to the merge).
-  auto run_piece = [&](int s_, const Piece& pc, int64_t f_, bool first) {
+  auto run_piece = [&](int s_, const Piece& pc, int64_t f_, bool first, const PageWindow& win) {
     const int b0 = int(f_ - pc.gs);
     const int b1 = int(min(int64_t(pc.nb), fend - pc.gs));
     if (first && lane == 0) {
@@ -339,7 +478,7 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
     const int pos = L - nq + (lane & 15) / G;  // position of this lane's row's query
     const RowKeys k{t_end, pos + 1, min(t_end, L - nq + 1), window_lo(pos, W), window_lo(L - 1, W)};
     run_range<KV, D, SMALLP, DENSE>(st, qf, qk_scale, static_cast<const char*>(a.cache.pool), bt, pc.blo + b0,
-                                    pc.blo + b1, k, L, a.cache.log2_page, Hkv * tile_b, pc.g * tile_b, lane);
+                                    pc.blo + b1, k, L, log2P, Hkv * tile_b, pc.g * tile_b, lane, &win);
     const bool complete = b0 == 0 && b1 == pc.nb;
     finish<D, G, ROWS>(st, a, pc.q0, nq, pc.g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale,
                        lane);
@@ -352,29 +491,59 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   // one L2 fetch serves several of them.  Each piece is computed exactly as in flat
   // order (same blocks, same record slots), so the results do not change.
   const int s_first = s;
-  const int64_t cum_first = cum;
   const Piece p_first = piece_of(s, cum, f0);
   const bool defer = f0 > p_first.gs && p_first.gs + p_first.nb < fend;
-  int64_t f = f0;
-  bool first = true;
+  bool tail = defer;  // the first piece still to be folded after the others
+  // current piece: sequence cs (cumulative blocks ccum), from flat block cf
+  int cs = s;
+  int64_t ccum = cum, cf = f0;
+  Piece cp = p_first;
+  bool cfirst = true, clast = false;
   if (defer) {
-    f = p_first.gs + p_first.nb;
+    cf = p_first.gs + p_first.nb;
     if (p_first.g + 1 == Hkv) {
-      cum += p_first.nb;
-      ++s;
+      ccum += p_first.nb;
+      ++cs;
     }
-    first = false;
+    cp = piece_of(cs, ccum, cf);
+    cfirst = false;
   }
-  while (f < fend) {
-    const Piece pc = piece_of(s, cum, f);
-    f = run_piece(s, pc, f, first);
-    first = false;
-    if (pc.g + 1 == Hkv) {
-      cum += pc.nb;
-      ++s;
+  PageWindow cw = window_of(cs, cp, cf);
+  for (;;) {
+    // the piece after this one, and its window, before this one is folded
+    int ns = cs;
+    int64_t ncum = ccum, nf = cp.gs + min(int64_t(cp.nb), fend - cp.gs);
+    if (cp.g + 1 == Hkv) {
+      ncum += cp.nb;
+      ++ns;
     }
+    bool has_next = !clast, nfirst = false, nlast = false;
+    Piece np = cp;
+    if (has_next) {
+      if (nf < fend) {
+        np = piece_of(ns, ncum, nf);
+      } else if (tail) {
+        ns = s_first;
+        np = p_first;
+        nf = f0;
+        nfirst = nlast = true;
+        tail = false;
+      } else {
+        has_next = false;
+      }
+    }
+    PageWindow nw{0, 0};
+    if (has_next) nw = window_of(ns, np, nf);
+    run_piece(cs, cp, cf, cfirst, cw);
+    if (!has_next) break;
+    cs = ns;
+    ccum = ncum;
+    cf = nf;
+    cp = np;
+    cfirst = nfirst;
+    clast = nlast;
+    cw = nw;
   }
-  if (defer) run_piece(s_first, p_first, f0, true);
 }
 
 // Merge of one cut (sequence, kv head) segment of the balanced schedule, by the

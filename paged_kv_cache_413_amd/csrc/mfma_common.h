@@ -190,12 +190,14 @@ struct PageWindow {
   int base;
 };
 
-// Load the window starting at logical page `base` of a table row with `npages`
-// valid entries (entries past them read as 0 and are never used).
+// Load the window starting at logical page `base` (< npages) of a table row with
+// `npages` valid entries.  Lanes past them repeat the last entry and are never used:
+// the load is unconditional, so nothing waits for it before its first use (a masked
+// load merged with a constant would make the wave wait right after issuing it).
 __device__ __forceinline__ void load_window(PageWindow& w, const int32_t* __restrict__ bt, int base,
                                             int npages, int lane) {
   w.base = base;
-  w.ids = base + lane < npages ? bt[base + lane] : 0;
+  w.ids = bt[min(base + lane, npages - 1)];
 }
 
 // Page of logical page p, which lies in the window.
@@ -995,7 +997,8 @@ __device__ __forceinline__ void pipeline_blocks(const char* __restrict__ pool, c
 template <int KV, int D, bool SMALLP, bool RAW = false, typename FoldFn>
 __device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const int32_t* __restrict__ bt,
                                            int b0, int b1, int L, int log2P, int64_t kv_stride_b,
-                                           int64_t head_off_b, int lane, FoldFn fold) {
+                                           int64_t head_off_b, int lane, FoldFn fold,
+                                           const PageWindow* win0 = nullptr) {
   if constexpr (SMALLP) {
     const PageWindow none{0, 0};
     pipeline_blocks<KV, D, true, RAW>(pool, bt, none, b0, b1, L, log2P, kv_stride_b, head_off_b, lane, fold);
@@ -1006,7 +1009,10 @@ __device__ __forceinline__ void run_blocks(const char* __restrict__ pool, const 
       const int base = c0 >> log2bp;
       const int c1 = min(b1, (base + 64) << log2bp);
       PageWindow win;
-      load_window(win, bt, base, npages, lane);
+      if (win0 && c0 == b0)
+        win = *win0;  // the caller's window of block b0's page (base b0 >> log2bp)
+      else
+        load_window(win, bt, base, npages, lane);
       pipeline_blocks<KV, D, false, RAW>(pool, bt, win, c0, c1, L, log2P, kv_stride_b, head_off_b, lane, fold);
       c0 = c1;
     }

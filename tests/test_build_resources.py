@@ -1,6 +1,6 @@
 """The build's kernel resource guard (host logic, no GPU): the compiler's per-kernel
-resource remarks are parsed, and scratch memory anywhere or LDS beyond the LDS-shared
-prefill kernel's three stages fails the build.  (A run-time index into a register array
+resource remarks are parsed, and scratch memory anywhere, LDS beyond the LDS-shared
+prefill kernel's three stages or LDS in a decode kernel fails the build.  (A run-time index into a register array
 once made the compiler move the MXFP4 staging registers to LDS: 94 208 bytes against the
 49 152 of the stages, and a 20 % slower prefill call.)"""
 from paged_kv_cache_413_amd import build as B
@@ -54,3 +54,12 @@ def test_stage_bytes_follow_head_dim():
     assert B._prefill_stage_lds("_ZN3pkv12_GLOBAL__N_118prefill_lds_kernelILi1ELi64ELi8EEEvNS_8AttnArgsE") == 24576
     assert B._prefill_stage_lds(PF) == 49152
     assert B._prefill_stage_lds(DEC) is None
+
+
+def test_lds_in_a_decode_kernel_fails():
+    """The decode kernels use no LDS: 4 608 bytes (72 per lane) appeared once when a
+    run-time chunk index into the per-wave sequence cache made the compiler move it there."""
+    u = B.parse_resource_remarks(REMARKS)
+    u[DEC]["LDS Size"] = "4608"
+    bad = B.check_resources(u)
+    assert len(bad) == 1 and "LDS 4608" in bad[0] and "uses none" in bad[0]

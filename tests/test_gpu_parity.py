@@ -234,9 +234,11 @@ def test_mfma_decode_edge_shapes(gpu_lib, P, lens, hq, hkv, D, ns):
     assert_lse_close(lse, ref[1], "bf16", f"P={P}")
 
 
-@pytest.mark.parametrize("kv,num_seqs,splits", [("bf16", 3000, 0), ("bf16", 3000, 2), ("fp8", 1000, 0)])
+@pytest.mark.parametrize("kv,num_seqs,splits", [("bf16", 3000, 0), ("bf16", 3000, 2), ("fp8", 1000, 0),
+                                                 ("bf16", 257, 0)])
 def test_many_short_sequences(gpu_lib, kv, num_seqs, splits):
-    """Thousands of decode sequences of 1..80 tokens (Llama-3-8B heads, pages of 64):
+    """Hundreds to thousands of decode sequences of 1..80 tokens (Llama-3-8B heads, pages
+    of 64; 257 is one past the sequences each balanced-kernel wave caches in registers):
     the balanced schedule's search over sequences runs many 64-sequence rounds and its
     shares hold many whole segments; fixed partitions give most sequences one."""
     from tests.device_batch import DeviceBatch
@@ -336,6 +338,10 @@ SHORT_CHUNKS = [
     (0, 32, [8, 5, 1, 7], [40, 300, 1200, 0], 16, 8, 64),                          # G = 2, D = 64
     (0, 128, [16, 3, 9], [129, 500, 31], 8, 8, 128),                               # G = 1, 16 queries
     (7, 64, [4, 4, 3, 1, 2], [3000, 800, 64, 1500, 90], 32, 8, 128),               # few waves: cut segments
+    # 300 sequences: past the first 256, whose lengths and query rows each wave of the
+    # balanced kernel keeps in registers, they are read from memory
+    (0, 32, np.random.RandomState(300).randint(1, 5, 300).tolist(),
+     np.random.RandomState(301).randint(0, 400, 300).tolist(), 32, 8, 128),
 ]
 
 
