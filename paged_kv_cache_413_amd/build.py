@@ -64,12 +64,12 @@ def parse_resource_remarks(text: str) -> dict:
     return out
 
 
-# LDS-shared prefill: three stages of one 32-token block of K and V in bf16 (2 x D x 32
+# LDS-shared prefill: five stages of one 32-token block of K and V in bf16 (2 x D x 32
 # x 2 bytes each); any more LDS than that is a register array the compiler moved to
 # LDS (a run-time index into it), which costs a store and a load per use.
 def _prefill_stage_lds(name: str):
     m = re.search(r"prefill_lds_kernelILi\d+ELi(\d+)ELi\d+E", name)
-    return 3 * 2 * int(m.group(1)) * 32 * 2 if m else None
+    return 5 * 2 * int(m.group(1)) * 32 * 2 if m else None
 
 
 # Kernels that use no LDS by design (the decode kernels hold everything in registers):

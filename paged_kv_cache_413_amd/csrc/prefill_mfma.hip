@@ -186,21 +186,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // ---- LDS-shared variant (pages of >= 32 tokens) -----------------------------------------
 // A workgroup of kPfWaves waves (one per SIMD, kPfTiles row tiles each) shares one K/V
 // stream: every 32-token block is fetched once per workgroup -- each thread loads its
-// 16-byte pieces of it into registers four blocks ahead (two register slots), then
-// writes them into one of three LDS stages two blocks ahead -- and each wave reads its
+// 16-byte pieces of it into registers five blocks ahead (two register slots), then
+// writes them into one of five LDS stages three blocks ahead -- and each wave reads its
 // MFMA operands from the stage with the same lane offsets as from the tile in HBM.  The
 // stage layout mirrors the block's HBM layout, in bf16: K as D/32 chunks of [32 tokens]
 // [32 dims], then V as [D][32 positions].  FP8 and MXFP4 blocks are decoded to bf16 as
 // they are staged, once per workgroup rather than once per wave that reads them (twice
-// the LDS bytes of an FP8 stage, a sixth of the conversions).  Three stages let a wave compute the scores of
-// block i+1 (matrix cores) while it runs the softmax of block i (vector ALU) and then
+// the LDS bytes of an FP8 stage, a sixth of the conversions).  A wave computes the scores
+// of block i+1 (matrix cores) while it runs the softmax of block i (vector ALU) and then
 // the P.V products of block i: the two units work at once within each wave, instead
-// of every wave waiting on one then the other between barriers.
+// of every wave waiting on one then the other between barriers.  Five stages let one
+// barrier serve two blocks: during a pair of steps the waves read the stages of three
+// blocks and write those of the next two (with three stages, one barrier per block:
+// 1 - 2 % slower on the mixed batch's prefill calls).
 #ifndef PKV_PF_TILES
 #define PKV_PF_TILES 2
 #endif
 constexpr int kPfTiles = PKV_PF_TILES;   // 16-row tiles per wave of the LDS-shared kernel
-constexpr int kPfStages = 3;
+constexpr int kPfStages = 5;             // LDS stages of 32-token blocks (bf16)
 #ifndef PKV_PF_SCHED
 #define PKV_PF_SCHED 2  // vector instructions the scheduler puts after each MFMA of a step (0: its own order)
 #endif
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   const int nblk = b1 - b0;
   // lane offset of the operand load in a K chunk / V tile (row n, segment c)
   const uint32_t lk = stage_lane_offset(lane);
-  // Raw scores of block b0+i (stage i%3) for the wave's tiles.
+  // Raw scores of block b0+i (stage i%5) for the wave's tiles.
   auto scores = [&](int i, float (&sc)[NT][8]) {
     const char* stg = smem + (i % kPfStages) * SL::BYTES;
     Block<D> b;
@@ -302,11 +305,13 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
 #pragma unroll
     for (int r = 0; r < NT; ++r) block_scores<D>(b, qf[r], sc[r]);
   };
-  // Step i: block i+2 goes from its register slot into stage (i+2)%3 -- last read (V
-  // of block i-1) before the previous step's barrier -- and the slot refills with block
-  // i+4 (clamped to the last block: a harmless repeat near the end).  The scores of
-  // block i+1 go into nxt (stage (i+1)%3, complete since the previous barrier; clamped
-  // at the end).  Then block i is folded: its scores (cur, from the previous step) are
+  // Step i: block i+3 goes from its register slot into stage (i+3)%5 -- that of block
+  // i-2, last read before the most recent barrier -- and the slot refills with block
+  // i+5 (clamped to the last block: a harmless repeat near the end).  The barrier comes
+  // after every odd step: within a pair of steps (2j, 2j+1) the waves read the stages of
+  // blocks 2j .. 2j+2 and write those of 2j+3 and 2j+4, five distinct stages.  The
+  // scores of block i+1 go into nxt (stage (i+1)%5, written two steps or more before,
+  // with a barrier since; clamped at the end).  Then block i is folded: its scores (cur, from the previous step) are
   // masked where the block reaches a row's position or lies past the wave's rows
   // (every weight there is 0, so such a block changes nothing), maxima and the rare
   // rescale vote come first, then the exponentials and P.V products of block i, which
@@ -324,10 +329,10 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   float sa_[NT][8], sb_[NT][8];
   auto step = [&](auto& rs, int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
     const int t = (b0 + i) << LOG2_BT;
-    const int blk2 = min(b0 + i + 2, last);
+    const int blk3 = min(b0 + i + 3, last);
     if constexpr (kFirst) { if (live) scores(min(i + 1, nblk - 1), nxt); }
-    stash_any(rs, (i + 2) % kPfStages, blk2);
-    fetch_any(rs, min(b0 + i + 4, last));
+    stash_any(rs, (i + 3) % kPfStages, blk3);
+    fetch_any(rs, min(b0 + i + 5, last));
     // a wave whose rows all lie past the chunk (short chunks) only stages its share
     if (live) {
     if constexpr (kEarlyScores) scores(min(i + 1, nblk - 1), nxt);
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     }
 #endif
     }
-    stage_barrier();
+    if (i & 1) stage_barrier();  // one barrier per two blocks
   };
   if (nblk > 0) {
     fetch_any(ra, b0);
@@ -372,15 +377,17 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
     fetch_any(ra, min(b0 + 2, last));
     stash_any(rb, 1, min(b0 + 1, last));
     fetch_any(rb, min(b0 + 3, last));
+    stash_any(ra, 2, min(b0 + 2, last));
+    fetch_any(ra, min(b0 + 4, last));
     stage_barrier();
     if (live) scores(0, sa_);
   }
   int i = 0;
   for (; i + 1 < nblk; i += 2) {
-    step(ra, i, sa_, sb_);      // slot ra holds the even blocks; scores alternate sa_/sb_
-    step(rb, i + 1, sb_, sa_);
+    step(rb, i, sa_, sb_);      // slot rb holds the odd blocks, ra the even; scores alternate sa_/sb_
+    step(ra, i + 1, sb_, sa_);
   }
-  if (i < nblk) step(ra, i, sa_, sb_);
+  if (i < nblk) step(rb, i, sa_, sb_);
   if (!live) return;
   prefill_finish<D, G, NT>(a, st, q0, C, cq0, g, split, qk_scale, vscale, lane, lsum);
 }
