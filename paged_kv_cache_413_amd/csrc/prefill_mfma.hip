@@ -207,6 +207,11 @@ constexpr int kPfStages = 5;             // LDS stages of 32-token blocks (bf16)
 #ifndef PKV_PF_SCHED
 #define PKV_PF_SCHED 2  // vector instructions the scheduler puts after each MFMA of a step (0: its own order)
 #endif
+// Per cache type: MXFP4 steps keep the scheduler's own order (its decoding conversions
+// already sit between the matrix instructions; with the interleave hint its prefill call
+// measured 191 against 186.5 us), bf16 and FP8 take the hint (equal or 1 % faster).
+template <int KV>
+constexpr int kPfSched = KV == DT_MXFP4 ? 0 : PKV_PF_SCHED;
 
 // Workgroup barrier; LDS writes and reads of this wave are complete before it.
 __device__ __forceinline__ void stage_barrier() {
@@ -316,26 +321,22 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
   // (every weight there is 0, so such a block changes nothing), maxima and the rare
   // rescale vote come first, then the exponentials and P.V products of block i, which
   // the scheduler interleaves.  Where the scores of block i+1 are issued decides what
-  // their matrix instructions overlap (measured on the mixed batch, prefill call):
-  // with bf16 and FP8 caches after the staging, under the dependent chain of row
-  // maxima (bf16 171-172 -> 166.5 us against issuing them with the exponentials, FP8
-  // unchanged); with MXFP4 before the staging, under its decoding conversions
-  // (226.9 -> 208.6 us).  Each cache measured slower with the other's order (bf16
-  // 174 us, MXFP4 242 us).
-  constexpr bool kFirst = KV == DT_MXFP4;          // scores(i+1) before the staging
-  constexpr bool kEarlyScores = KV != DT_MXFP4;    // scores(i+1) after it, before the maxima
+  // their matrix instructions overlap: first in the step, before the staging, they run
+  // under its LDS writes (and the MXFP4 decoding conversions).  Measured on the mixed
+  // batch's prefill call, against issuing them after the staging, before the maxima:
+  // bf16 165.0 against 169.8 us, FP8 172.7 against 173.5, MXFP4 182.9 against 186.4.
+  // (With one barrier per block the bf16 and FP8 calls had been faster the other way.)
   const int last = b1 - 1;
   typename SL::Regs ra, rb;
   float sa_[NT][8], sb_[NT][8];
   auto step = [&](auto& rs, int i, float (&cur)[NT][8], float (&nxt)[NT][8]) {
     const int t = (b0 + i) << LOG2_BT;
     const int blk3 = min(b0 + i + 3, last);
-    if constexpr (kFirst) { if (live) scores(min(i + 1, nblk - 1), nxt); }
+    if (live) scores(min(i + 1, nblk - 1), nxt);
     stash_any(rs, (i + 3) % kPfStages, blk3);
     fetch_any(rs, min(b0 + i + 5, last));
     // a wave whose rows all lie past the chunk (short chunks) only stages its share
     if (live) {
-    if constexpr (kEarlyScores) scores(min(i + 1, nblk - 1), nxt);
     if (t + BT > lim_min || t < lo_max) {  // wave-uniform: reaches a row's position or window start
 #pragma unroll
       for (int r = 0; r < NT; ++r)
@@ -359,14 +360,14 @@ __global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(k
       for (int dt = 0; dt < D / 16; ++dt) st[r].o[dt] = mma(pa[r].v, vv[dt], st[r].o[dt]);
       lsum[r] = mma(pa[r].v, ones, lsum[r]);  // the weights' row sums: P . 1 (one product per tile)
     }
-#if PKV_PF_SCHED
-    // exponentials and conversions of block i around the scores of block i+1
+    if constexpr (kPfSched<KV> > 0) {
+      // exponentials and conversions of block i around the scores of block i+1
 #pragma unroll
-    for (int k = 0; k < NT * D / 16; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x0002, PKV_PF_SCHED, 0);  // vector ALU
+      for (int k = 0; k < NT * D / 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x0002, kPfSched<KV>, 0);  // vector ALU
+      }
     }
-#endif
     }
     if (i & 1) stage_barrier();  // one barrier per two blocks
   };
