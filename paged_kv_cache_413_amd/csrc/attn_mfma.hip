@@ -203,8 +203,20 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
 }
 
 // ---- auto: contiguous equal shares of the flattened block space ------------------------
-// Flattened order: sequence-major, then kv head, then block; segment (s, g) covers
-// [Hkv*cum_s + g*nb_s, +nb_s) with nb_s = ceil(L_s / 32) and cum_s = sum_{s'<s} nb_s'.
+// Flattened order: sequence-major, then kv head, then block.  Each (sequence, kv head)
+// segment counts SC units more than its nb_s blocks: the cost of starting a segment (the
+// wave's pipeline drains, the queries and first blocks are loaded, the result is
+// written) in block times.  Segment (s, g) spans units [Hkv*cum_s + g*nu_s, +nu_s),
+// nu_s = nb_s + SC, cum_s = sum_{s'<s} nu_s'; its first SC units hold no block, and its
+// block k is unit Hkv*cum_s + g*nu_s + SC + k.  Waves take equal shares of units, so a
+// wave whose share holds many short segments holds fewer blocks.  Equal shares of blocks
+// alone left such waves behind (per-wave clocks, mixed batch: the last wave ended 47 us
+// after the median one).  SC per kernel, measured (decode call, us, SC = 0 / 2 / 3 / 4):
+// one wave per SIMD, bf16: Llama batch 98.1 / 97.7 / 99.1 / 99.5, mixed batch 301.2 /
+// 288.7 / 284.9 / 285.6 -> 2; two waves per SIMD: dense FP8 mixed batch 169.0 / 157.6 /
+// 155.0 / 153.5, MXFP4 Llama batch 40.0 / 39.4 / 38.8 / 38.4 -> 4.
+template <int KV, bool DENSE>
+constexpr int kSegCost = (KV == DT_MXFP4 || DENSE) ? 4 : 2;
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
@@ -223,6 +235,13 @@ __device__ __forceinline__ int seg_blocks(int L, int nq, int W, int& blo) {
   return ((L + BT - 1) >> LOG2_BT) - blo;
 }
 
+// Units of a segment in the flattened order: its blocks and its start cost SC.
+template <int SC>
+__device__ __forceinline__ int seg_units(int L, int nq, int W) {
+  int blo;
+  return seg_blocks(L, nq, W, blo) + SC;
+}
+
 // Queries of sequence s in this call: packed rows cu[s] .. cu[s+1]-1, or the one row s.
 __device__ __forceinline__ int queries_of(const int32_t* __restrict__ cu, int s) {
   return cu ? cu[s + 1] - cu[s] : 1;
@@ -237,7 +256,7 @@ __device__ __forceinline__ int64_t lane64(int64_t v, int l) {
 
 // Lengths (and, with several queries per sequence, the first packed row and the query
 // count) of the first kSeqCache sequences, one per lane and 64-sequence chunk, with the
-// inclusive running sum of their segment blocks.  A wave loads them once, every load
+// inclusive running sum of their segment units.  A wave loads them once, every load
 // issued before any is used; the share's location and each later segment's geometry
 // then come from registers (readlane) instead of a chain of dependent loads.  Sequences
 // past them are read from memory.
@@ -248,7 +267,7 @@ template <bool MQ>
 struct SeqCache {
   int L[kSeqChunks];
   int q0[MQ ? kSeqChunks : 1], nq[MQ ? kSeqChunks : 1];
-  int64_t incl[kSeqChunks];  // segment blocks (per kv head) of sequences 0 .. 64k + lane
+  int64_t incl[kSeqChunks];  // segment units (per kv head) of sequences 0 .. 64k + lane
   int64_t run;               // ... of all cached sequences
   int n;                     // cached sequences: min(S, kSeqCache)
 };
@@ -267,7 +286,7 @@ __device__ __forceinline__ int cached(const int (&v)[kSeqChunks], int s) {
   return r;
 }
 
-template <bool MQ>
+template <bool MQ, int SC>
 __device__ __forceinline__ void load_seqs(SeqCache<MQ>& c, const int32_t* __restrict__ lens,
                                           const int32_t* __restrict__ cu, int W, int S, int lane) {
   c.n = min(S, kSeqCache);
@@ -285,9 +304,8 @@ __device__ __forceinline__ void load_seqs(SeqCache<MQ>& c, const int32_t* __rest
   for (int k = 0; k < kSeqChunks; ++k) {
     if constexpr (MQ) c.nq[k] -= c.q0[k];
     if (64 * k < c.n) {  // wave-uniform
-      int blo;
-      const int64_t nb = 64 * k + lane < c.n ? int64_t(seg_blocks(c.L[k], MQ ? c.nq[k] : 1, W, blo)) : 0;
-      c.incl[k] = run + wave_incl_scan(nb, lane);
+      const int64_t nu = 64 * k + lane < c.n ? int64_t(seg_units<SC>(c.L[k], MQ ? c.nq[k] : 1, W)) : 0;
+      c.incl[k] = run + wave_incl_scan(nu, lane);
       run = lane64(c.incl[k], 63);
     } else {
       c.incl[k] = run;
@@ -319,23 +337,22 @@ __device__ __forceinline__ void seq_info(const SeqCache<MQ>& c, const int32_t* _
   }
 }
 
-// Total blocks of all (sequence, kv head) segments.
-template <bool MQ>
+// Total units of all (sequence, kv head) segments.
+template <bool MQ, int SC>
 __device__ __forceinline__ int64_t total_blocks(const SeqCache<MQ>& c, const int32_t* __restrict__ lens,
                                                 const int32_t* __restrict__ cu, int W, int S, int Hkv,
                                                 int lane) {
   int64_t sum = 0;
   if (S > kSeqCache) {  // wave-uniform
-    int blo;
-    for (int s = kSeqCache + lane; s < S; s += 64) sum += seg_blocks(lens[s], queries_of(cu, s), W, blo);
+    for (int s = kSeqCache + lane; s < S; s += 64) sum += seg_units<SC>(lens[s], queries_of(cu, s), W);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   }
   return uniform64((c.run + sum) * Hkv);
 }
 
-// Sequence whose segments contain flat block f, and its cum (blocks before it).
-template <bool MQ>
+// Sequence whose segments contain flat unit f, and its cum (units before it).
+template <bool MQ, int SC>
 __device__ __forceinline__ void locate(const SeqCache<MQ>& c, const int32_t* __restrict__ lens,
                                        const int32_t* __restrict__ cu, int W, int S, int Hkv, int64_t f,
                                        int lane, int& s_out, int64_t& cum_out) {
@@ -360,23 +377,22 @@ __device__ __forceinline__ void locate(const SeqCache<MQ>& c, const int32_t* __r
       const int64_t x = lane64(c.incl[j], first);
       incl = k == j ? x : incl;
     }
-    int L, q0, nq, blo;
+    int L, q0, nq;
     s_out = 64 * k + first;
     seq_info(c, lens, cu, s_out, L, q0, nq);
-    cum_out = incl - seg_blocks(L, nq, W, blo);
+    cum_out = incl - seg_units<SC>(L, nq, W);
     return;
   }
   int64_t run = c.run;
   for (int base = kSeqCache; base < S; base += 64) {
     const int s = base + lane;
-    int blo;
-    const int64_t nb = s < S ? int64_t(seg_blocks(lens[s], queries_of(cu, s), W, blo)) : 0;
-    const int64_t incl = wave_incl_scan(nb, lane);
+    const int64_t nu = s < S ? int64_t(seg_units<SC>(lens[s], queries_of(cu, s), W)) : 0;
+    const int64_t incl = wave_incl_scan(nu, lane);
     const uint64_t hit = __ballot(s < S && Hkv * (run + incl) > f);
     if (hit) {
       const int first = __builtin_ctzll(hit);
       s_out = base + first;
-      cum_out = uniform64(run + __shfl(incl - nb, first, 64));
+      cum_out = uniform64(run + __shfl(incl - nu, first, 64));
       return;
     }
     run = uniform64(run + __shfl(incl, 63, 64));
@@ -411,9 +427,11 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   const int32_t* cu = MQ ? a.cu_q_lens : nullptr;
   const int W = a.seqs.window;
   SeqCache<MQ> sc;
-  load_seqs(sc, lens, cu, W, S, lane);
-  const int64_t T = total_blocks(sc, lens, cu, W, S, Hkv, lane);
-  const int64_t share = max(int64_t(a.min_share), (T + a.num_waves - 1) / a.num_waves);
+  constexpr int SC = kSegCost<KV, DENSE>;
+  load_seqs<MQ, SC>(sc, lens, cu, W, S, lane);
+  const int64_t T = total_blocks<MQ, SC>(sc, lens, cu, W, S, Hkv, lane);
+  // (a share of more than SC units holds at least one block)
+  const int64_t share = max(int64_t(max(a.min_share, SC + 1)), (T + a.num_waves - 1) / a.num_waves);
   const int64_t f0 = int64_t(w) * share;
   int4* desc = a.ws_desc + w;
   if (f0 >= T) {
@@ -423,48 +441,59 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   const int64_t fend = min(T, f0 + share);
   int s;
   int64_t cum;
-  locate(sc, lens, cu, W, S, Hkv, f0, lane, s, cum);
+  locate<MQ, SC>(sc, lens, cu, W, S, Hkv, f0, lane, s, cum);
   const int64_t tile_b = tile_bytes(KV, a.cache.page_size, D);
   const int log2P = a.cache.log2_page;
-  // The piece of this wave's share in segment (s, g) that holds flat block f: its
-  // sequence geometry, and the flat block gs where the segment starts.
+  // The piece of this wave's share in segment (s, g) that holds flat unit f: its
+  // sequence geometry, the unit gs of the segment's first block, and the unit fs of the
+  // piece's first block (f, or gs when f lies in the segment's start cost).
   struct Piece {
     int L, q0, nq, blo, nb, g;
-    int64_t gs;
+    int64_t gs, fs;
   };
   auto piece_of = [&](int s_, int64_t cum_, int64_t f_) {
     Piece pc;
     seq_info(sc, lens, cu, s_, pc.L, pc.q0, pc.nq);
     pc.nb = seg_blocks(pc.L, pc.nq, W, pc.blo);
+    const int nu = pc.nb + SC;
     const int64_t seg0 = Hkv * cum_;
-    pc.g = int((f_ - seg0) / pc.nb);
-    pc.gs = seg0 + int64_t(pc.g) * pc.nb;
+    pc.g = int((f_ - seg0) / nu);
+    pc.gs = seg0 + int64_t(pc.g) * nu + SC;
+    pc.fs = max(f_, pc.gs);
     return pc;
+  };
+  // the sequence and cum of the segment after pc's
+  auto advance = [&](int& s_, int64_t& cum_, const Piece& pc) {
+    if (pc.g + 1 == Hkv) {
+      cum_ += pc.nb + SC;
+      ++s_;
+    }
   };
   // Block-table window of the piece's first page (pages of >= 32 tokens), loaded one
   // piece ahead: a wave that moves to its next segment then waits only for that
   // segment's first blocks, not for the table entries in front of them.
-  auto window_of = [&](int s_, const Piece& pc, int64_t f_) {
+  auto window_of = [&](int s_, const Piece& pc) {
     PageWindow win{0, 0};
     if constexpr (!SMALLP) {
-      const int first_blk = pc.blo + int(f_ - pc.gs);
+      const int first_blk = pc.blo + int(pc.fs - pc.gs);
       load_window(win, a.seqs.block_tables + int64_t(s_) * a.seqs.max_pages_per_seq,
                   first_blk >> (log2P - LOG2_BT), (pc.L + (1 << log2P) - 1) >> log2P, lane);
     }
     return win;
   };
-  // Fold the piece of segment (s, g) from flat block f to the segment's end or fend.
-  // `first`: the piece at f0 (the share's first, record slot 0, described to the merge).
-  auto run_piece = [&](int s_, const Piece& pc, int64_t f_, bool first, const PageWindow& win) {
-    const int b0 = int(f_ - pc.gs);
+  // Fold the piece of segment (s, g) from its first block to the segment's end or fend.
+  // `first`: the share's first piece (record slot 0, described to the merge).
+  auto run_piece = [&](int s_, const Piece& pc, bool first, const PageWindow& win) {
+    const int b0 = int(pc.fs - pc.gs);
     const int b1 = int(min(int64_t(pc.nb), fend - pc.gs));
     if (first && lane == 0) {
       // This wave merges its first segment when that segment started in an earlier
-      // wave (w0) and ends inside this one.  Record slot of w0: 1 unless the segment
-      // is w0's first too.
+      // wave (w0: the one whose share holds its first block) and ends inside this one.
+      // Record slot of w0: 0 if the segment is w0's first (w0's share starts at or
+      // after the segment's first unit), else 1.
       const int64_t w0 = pc.gs / share;
       const bool merges = pc.gs < f0 && pc.gs + pc.nb <= fend;
-      *desc = make_int4(s_, pc.g, int(w0), merges ? (1 | (pc.gs != w0 * share ? 2 : 0)) : 0);
+      *desc = make_int4(s_, pc.g, int(w0), merges ? (1 | (pc.gs - SC > w0 * share ? 2 : 0)) : 0);
     }
     float qk_scale, vscale;
     scales<KV>(a, pc.g, qk_scale, vscale);
@@ -482,63 +511,68 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
     const bool complete = b0 == 0 && b1 == pc.nb;
     finish<D, G, ROWS>(st, a, pc.q0, nq, pc.g, complete, int64_t(w) * 2 + (first ? 0 : 1), qk_scale, vscale,
                        lane);
-    return pc.gs + b1;
   };
   // Order of the pieces: a share whose first piece continues a segment begun in an
   // earlier wave folds that piece last, so every wave starts at the head of a segment.
   // The heads of neighbouring requests' segments are where a shared prefix lies: the
   // waves that read the same prefix pages then read them at about the same time, and
   // one L2 fetch serves several of them.  Each piece is computed exactly as in flat
-  // order (same blocks, same record slots), so the results do not change.
+  // order (same blocks, same record slots), so the results do not change.  A share
+  // starting in a segment's start cost begins at that segment's first block; one ending
+  // there holds none of that segment.
   const int s_first = s;
   const Piece p_first = piece_of(s, cum, f0);
-  const bool defer = f0 > p_first.gs && p_first.gs + p_first.nb < fend;
-  bool tail = defer;  // the first piece still to be folded after the others
-  // current piece: sequence cs (cumulative blocks ccum), from flat block cf
   int cs = s;
-  int64_t ccum = cum, cf = f0;
+  int64_t ccum = cum;
+  advance(cs, ccum, p_first);
   Piece cp = p_first;
-  bool cfirst = true, clast = false;
-  if (defer) {
-    cf = p_first.gs + p_first.nb;
-    if (p_first.g + 1 == Hkv) {
-      ccum += p_first.nb;
-      ++cs;
-    }
-    cp = piece_of(cs, ccum, cf);
-    cfirst = false;
+  bool later = p_first.gs + p_first.nb < fend;  // a piece after the first one holds blocks
+  if (later) {
+    cp = piece_of(cs, ccum, p_first.gs + p_first.nb);
+    later = cp.fs < fend;
   }
-  PageWindow cw = window_of(cs, cp, cf);
+  const bool defer = f0 > p_first.gs && later;
+  bool tail = defer;  // the first piece still to be folded after the others
+  bool cfirst = true, clast = !later;
+  if (defer) {
+    cfirst = false;
+  } else {
+    cs = s;
+    ccum = cum;
+    cp = p_first;
+  }
+  PageWindow cw = window_of(cs, cp);
   for (;;) {
     // the piece after this one, and its window, before this one is folded
     int ns = cs;
-    int64_t ncum = ccum, nf = cp.gs + min(int64_t(cp.nb), fend - cp.gs);
-    if (cp.g + 1 == Hkv) {
-      ncum += cp.nb;
-      ++ns;
-    }
+    int64_t ncum = ccum;
+    advance(ns, ncum, cp);
+    const int64_t nf = cp.gs + min(int64_t(cp.nb), fend - cp.gs);
     bool has_next = !clast, nfirst = false, nlast = false;
     Piece np = cp;
     if (has_next) {
-      if (nf < fend) {
+      bool flat = nf < fend;  // the next piece in flat order, if it holds blocks
+      if (flat) {
         np = piece_of(ns, ncum, nf);
-      } else if (tail) {
-        ns = s_first;
-        np = p_first;
-        nf = f0;
-        nfirst = nlast = true;
-        tail = false;
-      } else {
-        has_next = false;
+        flat = np.fs < fend;
+      }
+      if (!flat) {
+        if (tail) {
+          ns = s_first;
+          np = p_first;
+          nfirst = nlast = true;
+          tail = false;
+        } else {
+          has_next = false;
+        }
       }
     }
     PageWindow nw{0, 0};
-    if (has_next) nw = window_of(ns, np, nf);
-    run_piece(cs, cp, cf, cfirst, cw);
+    if (has_next) nw = window_of(ns, np);
+    run_piece(cs, cp, cfirst, cw);
     if (!has_next) break;
     cs = ns;
     ccum = ncum;
-    cf = nf;
     cp = np;
     cfirst = nfirst;
     clast = nlast;
