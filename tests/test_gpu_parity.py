@@ -303,6 +303,13 @@ AUTO_WAVES = [
                  head_dim=128, kv_dtype="fp8")),                   # fp8 dense, G = 2
     (1, 2, dict(lens=[1, 700, 33], page_size=64, num_q_heads=32, num_kv_heads=8,
                 head_dim=128)),                                    # one wave does it all
+    # shares of the least size (4 units; segments of 1 - 7 blocks plus a start cost of 2
+    # units), so share boundaries fall at every place in and around the start costs
+    (146, 2, dict(lens=[32] * 6 + [96] * 6 + [65, 200, 33, 130], page_size=32, num_q_heads=32,
+                  num_kv_heads=8, head_dim=128)),
+    # the same with two waves per SIMD (MXFP4: start cost 4, least share 5 units)
+    (168, 2, dict(lens=[32] * 6 + [96] * 6 + [65, 200, 33, 130], page_size=32, num_q_heads=32,
+                  num_kv_heads=8, head_dim=128, kv_dtype="mxfp4")),
 ]
 
 
