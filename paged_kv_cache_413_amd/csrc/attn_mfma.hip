@@ -213,10 +213,11 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
 // alone left such waves behind (per-wave clocks, mixed batch: the last wave ended 47 us
 // after the median one).  SC per kernel, measured (decode call, us, SC = 0 / 2 / 3 / 4):
 // one wave per SIMD, bf16: Llama batch 98.1 / 97.7 / 99.1 / 99.5, mixed batch 301.2 /
-// 288.7 / 284.9 / 285.6 -> 2; two waves per SIMD: dense FP8 mixed batch 169.0 / 157.6 /
-// 155.0 / 153.5, MXFP4 Llama batch 40.0 / 39.4 / 38.8 / 38.4 -> 4.
+// 288.7 / 284.9 / 285.6 -> 2; FP8: Llama-shaped batch - / 54.3 / 52.9 / 53.1 (the
+// shared-prefix batch flat) -> 3; two waves per SIMD: dense FP8 mixed batch 169.0 /
+// 157.6 / 155.0 / 153.5, MXFP4 Llama batch 40.0 / 39.4 / 38.8 / 38.4 -> 4.
 template <int KV, bool DENSE>
-constexpr int kSegCost = (KV == DT_MXFP4 || DENSE) ? 4 : 2;
+constexpr int kSegCost = (KV == DT_MXFP4 || DENSE) ? 4 : KV == DT_FP8 ? 3 : 2;
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
