@@ -197,8 +197,9 @@ size_t paged_attn_decode_workspace_size(const pkv_cache_t* cache, const pkv_seqs
  *   num_splits: 0 = the library partitions the keys itself: with a BF16 or FP8
  *         cache, BF16 queries and pages of >= 8 tokens, or an MXFP4 cache, BF16
  *         queries and pages of >= 32 tokens (the matrix-core kernels)
- *         the 32-token blocks of all (sequence, kv head) pairs are cut into equal
- *         contiguous shares, one per wave that fits on the device at once;
+ *         the 32-token blocks of all (sequence, kv head) pairs, each pair
+ *         counting a few blocks more for its start, are cut into equal contiguous
+ *         shares, one per wave that fits on the device at once;
  *         otherwise page-aligned partitions of at least 256 keys.  N > 0 = split
  *         each sequence's keys into page-aligned partitions of ceil(max_context_len
  *         / N) keys, rounded up to a page (and to 32 keys on the matrix-core

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
   finish<D, G, G>(st, a, s, 1, g, nsplit == 1, int64_t(sg) * a.max_splits + split, qk_scale, vscale, lane);
 }
 
-// ---- auto: contiguous equal shares of the flattened block space ------------------------
+// ---- auto: contiguous equal shares of the flattened blocks (and segment start costs) --
 // Flattened order: sequence-major, then kv head, then block.  Each (sequence, kv head)
 // segment counts SC units more than its nb_s blocks: the cost of starting a segment (the
 // wave's pipeline drains, the queries and first blocks are loaded, the result is
