@@ -215,9 +215,11 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
 // one wave per SIMD, bf16: Llama batch 98.1 / 97.7 / 99.1 / 99.5, mixed batch 301.2 /
 // 288.7 / 284.9 / 285.6 -> 2; FP8: Llama-shaped batch - / 54.3 / 52.9 / 53.1 (the
 // shared-prefix batch flat) -> 3; two waves per SIMD: dense FP8 mixed batch 169.0 /
-// 157.6 / 155.0 / 153.5, MXFP4 Llama batch 40.0 / 39.4 / 38.8 / 38.4 -> 4.
+// 157.6 / 155.0 / 153.5 (SC 6 / 8: 155.2 / 155.7) -> 4; MXFP4 Llama batch 40.0 / 39.4 /
+// 38.8 / 38.6 (SC 5 / 6: 39.3 / 39.0), MXFP4 mixed batch SC 4 / 5 / 6 / 8: 97.4 / 95.6 /
+// 93.7 / 95.2 -> 6.
 template <int KV, bool DENSE>
-constexpr int kSegCost = (KV == DT_MXFP4 || DENSE) ? 4 : KV == DT_FP8 ? 3 : 2;
+constexpr int kSegCost = KV == DT_MXFP4 ? 6 : DENSE ? 4 : KV == DT_FP8 ? 3 : 2;
 
 __device__ __forceinline__ int64_t wave_incl_scan(int64_t v, int lane) {
 #pragma unroll
