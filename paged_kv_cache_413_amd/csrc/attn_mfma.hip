@@ -588,7 +588,10 @@ __global__ __launch_bounds__(64 * kWgWaves) __attribute__((amdgpu_waves_per_eu(k
 // one cut segment: its first).  The pieces are in waves w0 .. w; the record of wave v
 // is slot 0, except slot 1 for w0 when the segment is not w0's first.  One workgroup
 // per wave (most find nothing to do and exit at once): a loop over several
-// descriptors per workgroup would chain their dependent loads.
+// descriptors per workgroup would chain their dependent loads.  The call is bound by
+// the launch and the two dependent loads (descriptor, then records): one wave per
+// descriptor, 128 threads (no LDS combine), or records touched before the descriptor
+// arrives all measured equal or slower.
 #ifndef PKV_AUTO_MERGE_THREADS
 #define PKV_AUTO_MERGE_THREADS 256
 #endif
